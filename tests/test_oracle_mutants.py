@@ -1,0 +1,84 @@
+"""Checker-mutation tests: plant a plausible mistake in a copy of the oracle
+(on the CPU), rebuild it, and require that the pins catch it.  This shows that
+the pins in oracle_pins.py can fail, and that each kind of mistake -- a
+dropped term, a wrong sign, an off-by-one index, a wrong operand slice, a
+wrong tie rule -- is covered."""
+import multiprocessing as mp
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle_pins as P  # noqa: E402
+from oracle import build as obuild  # noqa: E402
+
+SRC = open(obuild.SRC).read()
+
+# (id, original text, mutated text)
+MUTANTS = [
+    ("e4m3_bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3_int_subnormal", "(e == 0) ? (int64_t)m :", "(e == 0) ? (int64_t)(m + 1) :"),
+    ("relu_dropped", "if (x > 0.0) acc += x * wq;", "acc += x * wq;"),
+    ("qscale_ignored", "(q_scale ? (double)q_scale[r * H + h] : 1.0)", "1.0"),
+    ("kscale_ignored", "out[key] = (float)(acc * ksc);", "out[key] = (float)(acc);"),
+    ("window_off_by_one", "for (int64_t key = s; key < e; ++key) {\n      const uint8_t* kr",
+     "for (int64_t key = s + 1; key < e; ++key) {\n      const uint8_t* kr"),
+    ("k_transposed_index", "const uint8_t* kr = k + (b * N + key) * D;",
+     "const uint8_t* kr = k + (b * N + (N - 1 - key)) * D;"),
+    ("clamp_ke_missing", "  if (b > N) b = N;\n", "\n"),
+    ("tie_to_higher", "return (a->i > b->i) - (a->i < b->i);", "return (a->i < b->i) - (a->i > b->i);"),
+    ("topk_not_sorted", "qsort(o, (size_t)K, sizeof(int32_t), cmp_int_asc);", ";"),
+    ("topk_short_row_offset", "o[j] = (int32_t)(s + j);", "o[j] = (int32_t)j;"),
+    ("sink_dropped", "if (sink) den += exp(sk - mx);", ";"),
+    ("sink_scaled", "double sk = sink ? (double)sink[h] : -INFINITY;",
+     "double sk = sink ? sm_scale * (double)sink[h] : -INFINITY;"),
+    ("v_wrong_slice", "oh[c] += p * vr[c];", "oh[c] += p * vr[c + (Dqk - Dv)];"),
+    ("scale_ignored", "sc[j] = sm_scale * acc;", "sc[j] = acc;"),
+    ("minus_one_not_masked", "if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];",
+     "if (idx[j] < N) J[nj++] = idx[j] < 0 ? 0 : idx[j];"),
+    ("fp8_kv_scale_ignored", "(double)kv_scale[b * N + J[j]];", "1.0;"),
+]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(mutant_dir, name, orig, mut):
+    assert SRC.count(orig) == 1, f"mutation anchor for {name} not unique/found"
+    src = mutant_dir / f"{name}.c"
+    src.write_text(SRC.replace(orig, mut).replace(
+        '#include "dsa_oracle.h"', f'#include "{os.path.join(os.path.dirname(obuild.SRC), "dsa_oracle.h")}"'))
+    lib = str(mutant_dir / f"lib{name}.so")
+    obuild.build(out=lib, src=str(src), extra_flags=("-w",))
+    # A mutant may write out of bounds: run it in a forked child so it cannot
+    # corrupt this process.  A crash also counts as caught.
+    ctx = mp.get_context("fork")
+    rd, wr = ctx.Pipe(duplex=False)
+    proc = ctx.Process(target=_run_checks, args=(lib, wr))
+    proc.start()
+    wr.close()
+    try:
+        caught = rd.recv()
+    except EOFError:
+        caught = ["<crashed>"]
+    proc.join()
+    assert caught, f"no pin catches mutant {name}"
+
+
+def _run_checks(lib, conn):
+    import faulthandler
+    faulthandler.disable()  # a crashing mutant is expected; keep the log quiet
+    caught = []
+    with P.oracle_lib(lib):
+        for chk in P.ALL_CHECKS:
+            try:
+                chk()
+            except AssertionError:
+                caught.append(chk.__name__)
+    conn.send(caught)
+    conn.close()
+    os._exit(0)

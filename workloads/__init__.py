@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the DSA hot path.
+
+This module only draws and encodes input tensors; it holds none of the
+method's arithmetic (no scores, no selection, no softmax).  Both the GPU tests
+and the oracle are fed from here.
+
+Recipe (numpy PCG64 streams; every tensor has its own id -- 0 decode
+lengths, 1 indexer q, 2 indexer k, 3 indexer w, 4 attention q, 5 kv, 6 sink --
+and is drawn in chunks of 2^22 values, chunk c from
+Generator(PCG64(SeedSequence(seed, spawn_key=(id, c)))), so the values do not
+depend on how many threads fill them):
+  * indexer q and k: N(0,1) fp32, quantised to OCP e4m3fn per row with scale
+    amax/448 (x/scale clamped to +-448, round-to-nearest-even by torch's
+    float8_e4m3fn cast; an all-zero row gets scale 1);
+  * indexer weights w: N(0, w_std) fp32 with w_std = H^-1/2;
+  * attention q and kv: N(0,1) rounded to bf16 (RNE); for the fp8-KV workload
+    kv is quantised per row like the indexer k and a per-row fp32 scale kept;
+  * attn_sink: N(0,1) fp32, one per attention head;
+  * key windows: causal prefill ks = 0, ke = t+1; packed varlen ks = sequence
+    start, ke = t+1; decode ks = 0, ke = L_b with L_b uniform in
+    [4096, 65536], the query at the last position, keys >= L_b all zero.
+"""
+from dataclasses import dataclass, replace
+import math
+
+from concurrent.futures import ThreadPoolExecutor
+import os
+
+import numpy as np
+
+FP8_MAX = 448.0
+_CHUNK = 1 << 22  # values per generation chunk
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    M: int          # query tokens per batch entry
+    N: int          # keys per batch entry
+    H: int          # indexer heads
+    D: int          # indexer head dim
+    K: int          # top-k
+    Hq: int         # attention heads
+    Dqk: int        # attention q/kv dim
+    Dv: int         # attention output dim (first Dv dims of kv)
+    kv_fp8: bool = False
+    windows: str = "causal"   # causal | packed | decode
+    seg: int = 0              # packed: sequence length
+    decode_min: int = 4096
+    seed: int = 0
+
+    @property
+    def w_std(self):
+        return 1.0 / math.sqrt(self.H)
+
+    @property
+    def sm_scale(self):
+        return float(np.float32(1.0 / math.sqrt(self.Dqk)))
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+# The five workloads.  Sizes follow the DeepSeek-V3.2 shapes: indexer 64x128
+# fp8, top-k 2048, 128 attention heads over 576-wide latent KV (512 + 64 rope).
+WORKLOADS = {
+    "tiny_causal_256": Workload("tiny_causal_256", B=1, M=256, N=256, H=4, D=64,
+                                K=32, Hq=16, Dqk=64, Dv=64, seed=1),
+    "prefill_4096": Workload("prefill_4096", B=1, M=4096, N=4096, H=64, D=128,
+                             K=2048, Hq=128, Dqk=576, Dv=512, seed=2),
+    "varlen_4x8192": Workload("varlen_4x8192", B=1, M=32768, N=32768, H=64,
+                              D=128, K=2048, Hq=128, Dqk=576, Dv=512,
+                              windows="packed", seg=8192, seed=3),
+    "decode_b64": Workload("decode_b64", B=64, M=1, N=65536, H=64, D=128,
+                           K=2048, Hq=128, Dqk=576, Dv=512, windows="decode",
+                           seed=4),
+    "prefill_8192_fp8kv": Workload("prefill_8192_fp8kv", B=1, M=8192, N=8192,
+                                   H=32, D=128, K=2048, Hq=64, Dqk=576, Dv=512,
+                                   kv_fp8=True, seed=5),
+}
+
+
+def _gen(seed, tid, chunk):
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence(seed, spawn_key=(tid, chunk))))
+
+
+def _normal(seed, tid, shape, std=1.0):
+    """float32 N(0, std) of the given shape from tensor stream `tid`."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+
+    def fill(c):
+        s, e = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        _gen(seed, tid, c).standard_normal(e - s, dtype=np.float32, out=out[s:e])
+        if std != 1.0:
+            out[s:e] *= np.float32(std)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def quantize_e4m3fn_rows(x):
+    """Per-row (last axis) e4m3fn quantisation: returns (codes as torch
+    float8_e4m3fn tensor, fp32 scale per row)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    amax = t.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    y = (t / scale.unsqueeze(-1)).clamp_(-FP8_MAX, FP8_MAX)
+    return y.to(torch.float8_e4m3fn), scale.to(torch.float32)
+
+
+def to_bf16(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+
+
+def bounds(wl, rng=None, lengths=None):
+    """ks, ke int32 [B, M] and (decode) the per-batch lengths."""
+    B, M, N = wl.B, wl.M, wl.N
+    t = np.arange(M, dtype=np.int64)
+    if wl.windows == "causal":
+        ks = np.zeros((B, M), np.int32)
+        ke = np.broadcast_to((t + 1 + (N - M)).astype(np.int32), (B, M)).copy()
+    elif wl.windows == "packed":
+        ks = np.broadcast_to(((t // wl.seg) * wl.seg).astype(np.int32), (B, M)).copy()
+        ke = np.broadcast_to((t + 1).astype(np.int32), (B, M)).copy()
+    elif wl.windows == "decode":
+        assert lengths is not None
+        ks = np.zeros((B, M), np.int32)
+        ke = np.broadcast_to(lengths.reshape(B, 1).astype(np.int32), (B, M)).copy()
+    else:
+        raise ValueError(wl.windows)
+    return ks, ke
+
+
+def make_inputs(wl, parts=("indexer", "attn"), seed=None):
+    """Draw every input tensor of a workload.  Returns a dict of CPU tensors /
+    numpy arrays:
+      indexer: q8 [B,M,H,D] fp8, q_scale [B,M,H], k8 [B,N,D] fp8, k_scale [B,N],
+               w [B,M,H]
+      attn:    q [B,M,Hq,Dqk] bf16, kv [B,N,Dqk] bf16 or fp8 (+ kv_scale [B,N]),
+               sink [Hq] fp32
+      always:  ks, ke [B,M] int32 (numpy), lengths (decode) or None"""
+    import torch
+    seed = wl.seed if seed is None else seed
+    B, M, N = wl.B, wl.M, wl.N
+    lengths = None
+    if wl.windows == "decode":
+        lengths = _gen(seed, 0, 0).integers(wl.decode_min, N, size=B,
+                                            endpoint=True).astype(np.int64)
+    ks, ke = bounds(wl, lengths=lengths)
+    out = {"ks": ks, "ke": ke, "lengths": lengths}
+
+    def key_mask(x):
+        if lengths is not None:
+            for b in range(B):
+                x[b, lengths[b]:] = 0
+        return x
+
+    if "indexer" in parts:
+        q = _normal(seed, 1, (B, M, wl.H, wl.D))
+        out["q8"], out["q_scale"] = quantize_e4m3fn_rows(q)
+        del q
+        k = key_mask(_normal(seed, 2, (B, N, wl.D)))
+        out["k8"], out["k_scale"] = quantize_e4m3fn_rows(k)
+        del k
+        out["w"] = torch.from_numpy(_normal(seed, 3, (B, M, wl.H), wl.w_std))
+    if "attn" in parts:
+        qa = _normal(seed, 4, (B, M, wl.Hq, wl.Dqk))
+        out["q"] = to_bf16(qa)
+        del qa
+        kv = key_mask(_normal(seed, 5, (B, N, wl.Dqk)))
+        if wl.kv_fp8:
+            out["kv"], out["kv_scale"] = quantize_e4m3fn_rows(kv)
+        else:
+            out["kv"] = to_bf16(kv)
+            out["kv_scale"] = None
+        del kv
+        out["sink"] = torch.from_numpy(_normal(seed, 6, (wl.Hq,)))
+    return out
