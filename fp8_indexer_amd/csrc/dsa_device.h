@@ -1,0 +1,50 @@
+// dsa_device.h -- small device-side helpers shared by the libdsa kernels
+// (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// D = A*B + C on a 16x16 fp32 tile, A/B 16x128 OCP e4m3fn (32 bytes per lane).
+// Lane l holds A row (l%16), k-chunk [32*(l/16), +32); B likewise by column;
+// C lane l holds column l%16, rows 4*(l/16)+i.
+__device__ __forceinline__ f32x4 mfma_f8_16x16x128(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D = A*B + C on a 16x16 fp32 tile, A/B 16x32 bf16 (8 values per lane).
+// Lane l holds A row (l%16), k-chunk [8*(l/16), +8); C as above.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_xor(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+}  // namespace dsa

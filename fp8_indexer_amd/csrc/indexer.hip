@@ -1,0 +1,316 @@
+// indexer.hip -- FP8 lightning-indexer scores on gfx950.
+//
+// Computes, for every query token t and every key in its window [s, e)
+// (Modular "sparse_index_fp8_sm100_prefill" page, score formula; TileLang
+// "deepseek_v32" page, "Lightning Indexer"):
+//   logits[b,t,key] = k_scale[key] * sum_h relu(q[t,h,:].k[key,:]) * w[t,h] * q_scale[t,h]
+//
+// Design (MI355X-first):
+//  * Q-resident: a workgroup owns a block of TB query tokens; each of its 8
+//    waves keeps 128 (token, head) rows of q as MFMA A-fragments in VGPRs for
+//    the whole launch.  Keys stream through LDS in 64-key tiles, double
+//    buffered with a register prefetch, and every tile is shared by the 8
+//    waves.  The product S[(t,h), key] = q . k runs on the OCP-fp8 MFMA
+//    v_mfma_f32_16x16x128_f8f6f4 (one instruction covers a 128-deep dot).
+//  * The MFMA C layout puts 4 consecutive (t,h) rows of one token in each
+//    lane, so relu * w and most of the head sum are lane-local; the remaining
+//    sum over the 4 lane groups is two cross-lane butterflies per (token, key).
+//  * Work items are (token block, key chunk): a block only visits the chunks
+//    of its clamped window union [min s, max e) (range skipping for causal and
+//    packed variable-length inputs), and late token blocks, which have the
+//    longest windows, are dispatched first.  Item ids are laid out so that all
+//    chunks of one token block land on the same XCD, which keeps that block's
+//    q in one L2.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kIdxWaves = 8;
+constexpr int kIdxThreads = kIdxWaves * kWave;  // 512
+constexpr int kRowsPerWave = 128;               // (token, head) rows per wave
+constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
+constexpr int kKT = 64;                         // keys per LDS tile
+constexpr int kXcds = 8;
+
+template <int H, int D>
+struct IdxCfg {
+  static_assert(H == 4 || H == 8 || H == 16 || H == 32 || H == 64 || H == 128, "H");
+  static_assert(D == 64 || D == 128 || D == 256, "D");
+  static constexpr int TW = kRowsPerWave / H;  // tokens per wave
+  static constexpr int TB = TW * kIdxWaves;    // tokens per workgroup
+  static constexpr int KS = (D + 127) / 128;   // 128-deep MFMA steps
+  static constexpr int CPR = D / 16;           // 16-byte chunks per key row
+  static constexpr int TILE_BYTES = kKT * D;
+  static constexpr int CHUNKS = kKT * CPR;
+  static constexpr int CPT = (CHUNKS + kIdxThreads - 1) / kIdxThreads;
+};
+
+// Byte offset of logical 16-byte chunk c of key row kk inside an LDS tile:
+// chunks are XOR-swizzled by the row so that 16 lanes reading the same
+// logical chunk of 16 consecutive rows hit different banks.
+template <int D>
+__device__ __forceinline__ int tile_off(int kk, int c) {
+  constexpr int CPR = D / 16;
+  return kk * D + ((c ^ (kk % CPR)) << 4);
+}
+
+template <int H, int D>
+__global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
+    const float* __restrict__ w, const int* __restrict__ ks,
+    const int* __restrict__ ke, float* __restrict__ logits, int M, int N,
+    int n_tblocks, int n_tblocks_pad, int n_chunks, int chunk_keys) {
+  using C = IdxCfg<H, D>;
+  __shared__ __align__(16) uint8_t sK[2][C::TILE_BYTES];
+  __shared__ float sKs[2][kKT];
+  __shared__ int sRed[2][kIdxWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+
+  // ---- item id -> (batch, token block, key chunk), XCD-aware -------------
+  const int per_batch = n_tblocks_pad * n_chunks;
+  const int b = blockIdx.x / per_batch;
+  const int id = blockIdx.x % per_batch;
+  const int xcd = id % kXcds;
+  const int chunk = (id / kXcds) % n_chunks;
+  const int tb_rev = (id / (kXcds * n_chunks)) * kXcds + xcd;
+  const int tb = n_tblocks_pad - 1 - tb_rev;  // latest tokens first
+  if (tb < 0 || tb >= n_tblocks) return;
+  const int t0 = tb * C::TB;
+
+  // ---- window union of the block: [kmin, kmax) ---------------------------
+  int smin = N, emax = 0;
+  for (int i = tid; i < C::TB; i += kIdxThreads) {
+    const int t = t0 + i;
+    if (t < M) {
+      const int r = b * M + t;
+      const int s = clampi(ks[r], 0, N);
+      const int e = clampi(ke[r], s, N);
+      if (e > s) {
+        smin = min(smin, s);
+        emax = max(emax, e);
+      }
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    smin = min(smin, __shfl_xor(smin, m, kWave));
+    emax = max(emax, __shfl_xor(emax, m, kWave));
+  }
+  if (lane == 0) {
+    sRed[0][wave] = smin;
+    sRed[1][wave] = emax;
+  }
+  __syncthreads();
+  int kmin = sRed[0][0], kmax = sRed[1][0];
+#pragma unroll
+  for (int i = 1; i < kIdxWaves; ++i) {
+    kmin = min(kmin, sRed[0][i]);
+    kmax = max(kmax, sRed[1][i]);
+  }
+  const int c0 = kmin + chunk * chunk_keys;
+  if (kmin >= kmax || c0 >= kmax) return;  // uniform across the workgroup
+  const int c1 = min(kmax, c0 + chunk_keys);
+
+  // ---- this wave's tokens: q fragments, effective weights, windows -------
+  const int tw0 = t0 + wave * C::TW;
+  i32x8 qf[kRT][C::KS];
+  float weff[kRT][4];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int row = rt * 16 + col;
+    const int t = tw0 + row / H, h = row % H;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int d0 = s * 128 + g * 32;
+      i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t < M && d0 < D) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(q + ((size_t)(b * M + t) * H + h) * D + d0);
+        const i32x4 lo = p[0], hi = p[1];
+        v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      qf[rt][s] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r2 = rt * 16 + g * 4 + i;
+      const int t2 = tw0 + r2 / H, h2 = r2 % H;
+      float we = 0.f;
+      if (t2 < M) {
+        const size_t o = (size_t)(b * M + t2) * H + h2;
+        we = w[o] * (q_scale ? q_scale[o] : 1.f);
+      }
+      weff[rt][i] = we;
+    }
+  }
+  int ws[C::TW], we_[C::TW];
+  int wmin = N, wmax = 0;
+#pragma unroll
+  for (int tl = 0; tl < C::TW; ++tl) {
+    const int t = tw0 + tl;
+    int s = 0, e = 0;
+    if (t < M) {
+      const int r = b * M + t;
+      s = clampi(ks[r], 0, N);
+      e = clampi(ke[r], s, N);
+    }
+    // restrict to this chunk so that zero-filled keys are never written
+    s = max(s, c0);
+    e = min(e, c1);
+    ws[tl] = s;
+    we_[tl] = e;
+    if (e > s) {
+      wmin = min(wmin, s);
+      wmax = max(wmax, e);
+    }
+  }
+
+  // ---- K tile staging -----------------------------------------------------
+  const int ntiles = (c1 - c0 + kKT - 1) / kKT;
+  i32x4 pre[C::CPT];
+  float pks = 0.f;
+  auto gload = [&](int tile) {
+    const int kb = c0 + tile * kKT;
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      const int ch = tid + j * kIdxThreads;
+      i32x4 v = {0, 0, 0, 0};
+      if (ch < C::CHUNKS) {
+        const int key = kb + ch / C::CPR;
+        if (key < c1)
+          v = *reinterpret_cast<const i32x4*>(k + ((size_t)b * N + key) * D + (ch % C::CPR) * 16);
+      }
+      pre[j] = v;
+    }
+    if (tid < kKT) {
+      const int key = kb + tid;
+      pks = key < c1 ? k_scale[(size_t)b * N + key] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      const int ch = tid + j * kIdxThreads;
+      if (ch < C::CHUNKS)
+        *reinterpret_cast<i32x4*>(&sK[buf][tile_off<D>(ch / C::CPR, ch % C::CPR)]) = pre[j];
+    }
+    if (tid < kKT) sKs[buf][tid] = pks;
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int kb = c0 + tile * kKT;
+    if (tile + 1 < ntiles) gload(tile + 1);
+    // skip waves whose tokens do not see this tile
+    if (wmax > kb && wmin < kb + kKT) {
+#pragma unroll 1
+      for (int n = 0; n < kKT / 16; ++n) {
+        const int kk = n * 16 + col;
+        f32x4 acc[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          i32x8 bf = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (s * 128 + g * 32 < D) {
+            const int c = s * 8 + g * 2;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(&sK[buf][tile_off<D>(kk, c)]);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(&sK[buf][tile_off<D>(kk, c + 1)]);
+            bf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma_f8_16x16x128(qf[rt][s], bf, acc[rt]);
+        }
+        // epilogue: relu * weight, sum over heads, * k_scale, masked store
+        const float ksc = sKs[buf][kk];
+        const int key = kb + kk;
+        float* out_col = logits + (size_t)key;
+        if constexpr (H >= 16) {
+          constexpr int TPT = H / 16;  // MFMA tiles per token
+#pragma unroll
+          for (int tl = 0; tl < C::TW; ++tl) {
+            float sum = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < TPT; ++rr) {
+              const int rt = tl * TPT + rr;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
+            }
+            sum += wave_xor(sum, 16);
+            sum += wave_xor(sum, 32);
+            if ((tl & 3) == g && key >= ws[tl] && key < we_[tl])
+              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
+          }
+        } else if constexpr (H == 8) {
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
+            sum += wave_xor(sum, 16);
+            const int tl = rt * 2 + (g >> 1);
+            if ((g & 1) == 0 && key >= ws[tl] && key < we_[tl])
+              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
+          }
+        } else {  // H == 4: one token per lane group
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
+            const int tl = rt * 4 + g;
+            if (key >= ws[tl] && key < we_[tl])
+              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
+          }
+        }
+      }
+    }
+    if (tile + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+template <int H, int D>
+hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
+  using C = IdxCfg<H, D>;
+  const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
+  const int n_tblocks_pad = (n_tblocks + kXcds - 1) / kXcds * kXcds;
+  // Key chunk: at least 512 keys, at most 16 chunks over the key axis.
+  int chunk_keys = (int)((a.N + 15) / 16);
+  chunk_keys = max(512, (chunk_keys + kKT - 1) / kKT * kKT);
+  const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
+  const long long blocks = (long long)a.B * n_tblocks_pad * n_chunks;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((indexer_logits_kernel<H, D>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
+                     stream, (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
+                     a.ks, a.ke, a.logits, (int)a.M, (int)a.N, n_tblocks, n_tblocks_pad, n_chunks,
+                     chunk_keys);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_supported(int H, int D) {
+  const bool h = H == 4 || H == 8 || H == 16 || H == 32 || H == 64 || H == 128;
+  const bool d = D == 64 || D == 128 || D == 256;
+  return h && d;
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
+#define DSA_IDX_CASE(HH, DD) \
+  if (a.H == HH && a.D == DD) return launch<HH, DD>(a, stream);
+#define DSA_IDX_H(HH) DSA_IDX_CASE(HH, 64) DSA_IDX_CASE(HH, 128) DSA_IDX_CASE(HH, 256)
+  DSA_IDX_H(4) DSA_IDX_H(8) DSA_IDX_H(16) DSA_IDX_H(32) DSA_IDX_H(64) DSA_IDX_H(128)
+#undef DSA_IDX_H
+#undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

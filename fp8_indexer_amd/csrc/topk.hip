@@ -1,0 +1,197 @@
+// topk.hip -- exact per-row top-k on gfx950.
+//
+// Method (TileLang "deepseek_v32" page, "Top-k Selector"): floats become
+// order-preserving unsigned keys; a histogram of the leading key bits and a
+// cumulative sum locate the bin that holds the K-th largest value; only that
+// bin is refined on the next bits, so the exact threshold is found without
+// sorting the row.  Here the 32-bit key is resolved in three MSD rounds of
+// 12, 10 and 10 bits with LDS histograms (4096 / 1024 bins).
+//
+// Selection rule (this library's contract): the K keys of [s, e) first in
+// (value descending, index ascending) order, with -0 == +0 and NaN ranked as
+// -inf, written in ascending index order.  After the rounds the exact K-th
+// key tau and the number of keys strictly above it are known; the emission
+// pass walks the row in index order, 512 keys at a time, and uses wavefront
+// ballots plus a block prefix sum to place every key > tau, and the first
+// (K - #above) keys == tau, at their ascending output slot.  No atomics touch
+// the output, so it is deterministic.
+//
+// One 512-thread workgroup per row.  Rows up to 8192 keys are read from HBM
+// once and kept in VGPRs (16 keys per lane); longer rows are re-read from L2
+// on each pass.  Rows with len <= K only write s..e-1 and -1 padding.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kTkThreads = 512;
+constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kEPT = 16;  // register-resident keys per lane
+
+// Order-preserving key: larger float -> larger unsigned key.  NaN -> key of
+// -inf; -0 -> key of +0.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) b = 0xFF800000u;  // NaN -> -inf
+  if (b == 0x80000000u) b = 0u;                           // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive prefix sum over the 512 threads of the block (thread order).
+__device__ __forceinline__ int block_excl_scan(int v, int& total, int* sWave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sWave[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTkWaves; ++i) {
+    const int t = sWave[i];
+    pre += i < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ logits,
+                                                          const int* __restrict__ ks,
+                                                          const int* __restrict__ ke,
+                                                          int* __restrict__ out, int N, int K) {
+  __shared__ uint32_t hist[4096];
+  __shared__ int sWave[kTkWaves];
+  __shared__ int sCnt[2][kTkWaves];
+  __shared__ int sSel[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t r = blockIdx.x;
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  const int len = e - s;
+  int* o = out + r * (size_t)K;
+
+  if (len <= K) {  // short row: the whole window, then -1 padding
+    for (int i = tid; i < K; i += kTkThreads) o[i] = i < len ? s + i : -1;
+    return;
+  }
+
+  const float* row = logits + r * (size_t)N;
+  const int nch = (len + kTkThreads - 1) / kTkThreads;
+  const bool resident = nch <= kEPT;
+  uint32_t keys[kEPT];
+  if (resident) {
+#pragma unroll
+    for (int c = 0; c < kEPT; ++c) {
+      const int i = s + c * kTkThreads + tid;
+      keys[c] = (c < nch && i < e) ? order_key(row[i]) : 0u;
+    }
+  }
+  auto get = [&](int c) -> uint32_t {
+    if (resident) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < kEPT; ++j) v = (j == c) ? keys[j] : v;
+      return v;
+    }
+    const int i = s + c * kTkThreads + tid;
+    return i < e ? order_key(row[i]) : 0u;
+  };
+
+  // ---- three MSD rounds: 12 + 10 + 10 key bits ---------------------------
+  uint32_t prefix = 0;
+  int krem = K, above_total = 0;
+#pragma unroll 1
+  for (int round = 0; round < 3; ++round) {
+    const int shift = round == 0 ? 20 : (round == 1 ? 10 : 0);
+    const int nbins = round == 0 ? 4096 : 1024;
+    const int pshift = shift + (round == 0 ? 12 : 10);  // bits above this digit
+    for (int i = tid; i < nbins; i += kTkThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      const int i = s + c * kTkThreads + tid;
+      const uint32_t u = get(c);
+      const bool match = i < e && (round == 0 || (u >> pshift) == prefix);
+      if (match) atomicAdd(&hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    // suffix counts: thread t owns bins [t*bpt, (t+1)*bpt)
+    const int bpt = nbins / kTkThreads;
+    int tsum = 0;
+    for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
+    int total;
+    const int pre = block_excl_scan(tsum, total, sWave);
+    int above = total - pre - tsum;  // keys in bins owned by higher threads
+    for (int j = bpt - 1; j >= 0; --j) {
+      const int c = (int)hist[tid * bpt + j];
+      if (above < krem && krem <= above + c) {
+        sSel[0] = tid * bpt + j;
+        sSel[1] = above;
+      }
+      above += c;
+    }
+    __syncthreads();
+    const int bin = sSel[0], ab = sSel[1];
+    prefix = (prefix << (round == 0 ? 12 : 10)) | (uint32_t)bin;
+    krem -= ab;
+    above_total += ab;
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;
+  const int n_eq = K - above_total;  // keys equal to tau that are selected (>= 1)
+
+  // ---- emission in index order -------------------------------------------
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_run = 0, sel_run = 0;
+#pragma unroll 1
+  for (int c = 0; c < nch; ++c) {
+    const int i = s + c * kTkThreads + tid;
+    const uint32_t u = get(c);
+    const bool valid = i < e;
+    const bool gt = valid && u > tau;
+    const bool eq = valid && u == tau;
+    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+    if (lane == 0) {
+      sCnt[0][wave] = __popcll(mgt);
+      sCnt[1][wave] = __popcll(meq);
+    }
+    __syncthreads();
+    int gt_off = 0, eq_off = 0, gt_tot = 0, eq_tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+      const int a = sCnt[0][w], b = sCnt[1][w];
+      gt_off += w < wave ? a : 0;
+      eq_off += w < wave ? b : 0;
+      gt_tot += a;
+      eq_tot += b;
+    }
+    const int gt_before = gt_off + __popcll(mgt & lt_mask);
+    const int eq_before = eq_off + __popcll(meq & lt_mask);
+    const int eq_left = max(0, n_eq - eq_run);
+    const bool eq_sel = eq && eq_before < eq_left;
+    const int pos = sel_run + gt_before + min(eq_before, eq_left);
+    if ((gt || eq_sel) && pos < K) o[pos] = i;  // pos < K always; guard is defensive
+    sel_run += gt_tot + min(eq_tot, eq_left);
+    eq_run += eq_tot;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+  const long long rows = a.B * a.M;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a.logits,
+                     a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

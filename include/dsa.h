@@ -1,0 +1,197 @@
+/*
+ * dsa.h -- C ABI of libdsa: the DeepSeek-style sparse-attention (DSA) hot
+ * path on AMD Instinct MI355X (gfx950).
+ *
+ *   1. dsa_indexer_logits  -- FP8 lightning-indexer scores
+ *   2. dsa_topk            -- exact per-row top-k over those scores
+ *   3. dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink
+ *   4. dsa_prefill         -- 1 -> 2 -> 3 on one stream
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Tensor arguments are DEVICE pointers to dense row-major arrays (the last
+ *    dimension is contiguous).  Pointers must be 16-byte aligned, except the
+ *    per-row scale, weight, bound and sink arrays, which need 4-byte alignment.
+ *  * Every call only ENQUEUES work on `stream` (a hipStream_t, NULL = the
+ *    default stream) and returns; there is no host synchronisation unless the
+ *    environment variable DSA_SYNC_CHECK=1 is set, in which case the call
+ *    waits for its kernels and reports their errors.
+ *  * Ownership: the caller allocates and owns every buffer, including the
+ *    intermediates of dsa_prefill.  The library keeps no pointer after a call
+ *    returns and allocates no device memory.  Calls are thread-safe.
+ *  * Errors: arguments are checked on the host before anything is enqueued.
+ *    NULL pointers, non-positive sizes, misalignment or inconsistent sizes
+ *    give DSA_ERR_INVALID_VALUE; a valid shape with no compiled kernel gives
+ *    DSA_ERR_NOT_SUPPORTED.  In both cases nothing is launched and no output
+ *    is written.  A failed launch gives DSA_ERR_LAUNCH.
+ *  * Device-side data contracts are clamped or masked, never trapped: bounds
+ *    are clamped, out-of-range indices are treated as -1.
+ *  * FP8 means OCP float8 e4m3fn (1 sign, 4 exponent bits with bias 7, 3
+ *    mantissa bits, largest finite 448, 0x7F/0xFF NaN).  NaN codes are not
+ *    valid inputs; results that depend on them are unspecified.
+ *  * bf16 is the upper half of an IEEE binary32.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_VERSION 100 /* 1.0.0 */
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_VALUE = 1,
+  DSA_ERR_NOT_SUPPORTED = 2,
+  DSA_ERR_LAUNCH = 3
+} dsa_status;
+
+typedef enum dsa_kv_dtype {
+  DSA_KV_BF16 = 0,       /* kv holds bf16 values                             */
+  DSA_KV_FP8_E4M3FN = 1  /* kv holds e4m3fn codes; value = code * kv_scale   */
+} dsa_kv_dtype;
+
+/*
+ * dsa_indexer_logits -- lightning-indexer scores.
+ *
+ * Defined by the Modular "sparse_index_fp8_sm100_prefill" page (score
+ * formula, with the per-(token, head) query scale in the weight position) and
+ * the TileLang "deepseek_v32" examples page, section "Lightning Indexer"
+ * (relu, head weights, key scale, sum over heads, per-token key bounds):
+ *
+ *   logits[b,t,key] = k_scale[b,key] *
+ *        sum_h relu( sum_d q[b,t,h,d] * k[b,key,d] ) * weights[b,t,h] * q_scale[b,t,h]
+ *
+ * for every key in [s, e) with s = clamp(ks[b,t], 0, N), e = clamp(ke[b,t], s, N).
+ *
+ *   q        [B, M, H, D]  e4m3fn codes (1 byte each)
+ *   q_scale  [B, M, H]     fp32, or NULL for 1 (may also be folded into
+ *                          weights by the caller: relu(s*x) = s*relu(x), s > 0)
+ *   k        [B, N, D]     e4m3fn codes
+ *   k_scale  [B, N]        fp32
+ *   weights  [B, M, H]     fp32
+ *   ks, ke   [B, M]        int32 per-token key bounds
+ *   logits   [B, M, N]     fp32 output.  Only keys inside each token's window
+ *                          are written; entries outside it are left untouched
+ *                          (unspecified to the caller).
+ * Supported: H in {4, 8, 16, 32, 64, 128}, D in {64, 128, 256}; N < 2^31.
+ * Products are exact and accumulate in fp32; the head sum is fp32.
+ */
+dsa_status dsa_indexer_logits(const void* q, const float* q_scale,
+                              const void* k, const float* k_scale,
+                              const float* weights, const int32_t* ks,
+                              const int32_t* ke, float* logits, int64_t B,
+                              int64_t M, int64_t N, int32_t H, int32_t D,
+                              void* stream);
+
+/*
+ * dsa_topk -- exact top-k per row.
+ *
+ * Defined by the TileLang "deepseek_v32" examples page, section "Top-k
+ * Selector" (exact selection over each row's [start, end) without a full
+ * sort; indices are absolute key positions).  For row (b,t) with window
+ * [s, e) clamped as in dsa_indexer_logits and len = e - s:
+ *   * len <= K: the output is s, s+1, ..., e-1 followed by -1s (the logits
+ *     are not read);
+ *   * len  > K: the output is the K keys of [s, e) that come first in the
+ *     order (value descending, index ascending) -- ties go to the lower index,
+ *     -0 equals +0, NaN ranks as -inf -- in ascending index order.
+ *
+ *   logits     [B, M, N] fp32 (only each row's window is read)
+ *   ks, ke     [B, M]    int32
+ *   topk_idxs  [B, M, K] int32 output
+ * Supported: 1 <= K <= 4096, N < 2^31.  Output is deterministic.
+ */
+dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
+                    int32_t* topk_idxs, int64_t B, int64_t M, int64_t N,
+                    int32_t K, void* stream);
+
+/*
+ * dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink.
+ *
+ * Defined by the DeepSeek V4.1 atlas page, sparse_attn_kernel and its wrapper
+ * sparse_attn (gather the top-k KV rows by index, online softmax, per-head
+ * attn_sink added to the denominator only, -1 indices masked, a row without
+ * a valid index gives zero), with the value read from the first Dv columns
+ * of the shared latent KV row.  For each (b, t, h), J = the indices j of
+ * topk_idxs[b,t,:] with 0 <= j < N (others are skipped like -1):
+ *   s_j  = sm_scale * sum_{d < Dqk} q[b,t,h,d] * kv[b,j,d]
+ *   o[b,t,h,c] = sum_j exp(s_j) kv[b,j,c] / (sum_j exp(s_j) + exp(attn_sink[h]))
+ * for c < Dv (the sink term is absent when attn_sink is NULL); o = 0 if J is
+ * empty.  Softmax runs in base 2 with sm_scale*log2(e) folded in, in fp32;
+ * QK^T and PV use bf16 MFMA with fp32 accumulation (P rounded to bf16).
+ *
+ *   q          [B, M, Hq, Dqk] bf16
+ *   kv         [B, N, Dqk]     bf16, or e4m3fn codes (kv_dtype = FP8)
+ *   kv_scale   [B, N] fp32 per-row scale for FP8 kv; must be NULL for bf16
+ *   attn_sink  [Hq] fp32 or NULL
+ *   topk_idxs  [B, M, K] int32
+ *   o          [B, M, Hq, Dv] bf16 output
+ *   sm_scale   softmax scale; <= 0 selects 1/sqrt(Dqk)
+ * Supported: Hq a multiple of 16 up to 256; (Dqk, Dv) in {(64, 64), (576, 512)};
+ * 1 <= K <= 4096; Dv <= Dqk.
+ */
+dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
+                               dsa_kv_dtype kv_dtype, const float* kv_scale,
+                               const float* attn_sink,
+                               const int32_t* topk_idxs, void* o, int64_t B,
+                               int64_t M, int64_t N, int32_t Hq, int32_t Dqk,
+                               int32_t Dv, int32_t K, float sm_scale,
+                               void* stream);
+
+/*
+ * dsa_prefill -- the whole path on one stream: indexer scores into `logits`,
+ * top-k into `topk_idxs`, sparse attention into `o`.  Every field has the
+ * meaning, layout and constraints of the same argument above; `logits` and
+ * `topk_idxs` are caller-owned intermediates that hold the stage results when
+ * the stream reaches the end of the call.  The argument struct is read during
+ * the call only.
+ */
+typedef struct dsa_prefill_args {
+  /* sizes */
+  int64_t batch;       /* B */
+  int64_t seq_q;       /* M: query tokens per batch entry */
+  int64_t seq_kv;      /* N: keys per batch entry */
+  /* indexer */
+  const void* index_q;        /* [B, M, H, D] e4m3fn */
+  const float* index_q_scale; /* [B, M, H] or NULL */
+  const void* index_k;        /* [B, N, D] e4m3fn */
+  const float* index_k_scale; /* [B, N] */
+  const float* index_weights; /* [B, M, H] */
+  const int32_t* ks;          /* [B, M] */
+  const int32_t* ke;          /* [B, M] */
+  int32_t index_heads;        /* H */
+  int32_t index_dim;          /* D */
+  /* top-k */
+  int32_t topk;               /* K */
+  /* attention */
+  const void* q;              /* [B, M, Hq, Dqk] bf16 */
+  const void* kv;             /* [B, N, Dqk] */
+  dsa_kv_dtype kv_dtype;
+  const float* kv_scale;      /* [B, N] (FP8 kv) or NULL */
+  const float* attn_sink;     /* [Hq] or NULL */
+  void* o;                    /* [B, M, Hq, Dv] bf16 */
+  int32_t heads;              /* Hq */
+  int32_t dqk;                /* Dqk */
+  int32_t dv;                 /* Dv */
+  float sm_scale;             /* <= 0 -> 1/sqrt(Dqk) */
+  /* caller-owned intermediates */
+  float* logits;              /* [B, M, N] */
+  int32_t* topk_idxs;         /* [B, M, K] */
+} dsa_prefill_args;
+
+dsa_status dsa_prefill(const dsa_prefill_args* args, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* dsa_status_string(dsa_status s);
+
+/* DSA_VERSION of the built library. */
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

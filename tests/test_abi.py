@@ -1,0 +1,142 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, the ctypes struct matches the C layout, and invalid arguments are
+rejected on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_indexer_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        pytest.skip("libdsa.so not built")
+    return dsa.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_stages():
+    fns = header_functions()
+    for f in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_attn_fwd", "dsa_prefill",
+              "dsa_status_string", "dsa_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for f in header_functions():
+        assert hasattr(L, f), f"libdsa.so does not export {f}"
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for f in header_functions():
+        assert re.search(rf"\bT {f}\b", out), f
+
+
+def test_version_and_status_strings():
+    L = _lib()
+    assert dsa.version() == 100
+    for s in range(4):
+        assert L.dsa_status_string(s)
+    assert b"unknown" in L.dsa_status_string(99)
+
+
+def test_prefill_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in dsa.PrefillArgs._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "dsa.h"\nint main(void){\n'
+                    + 'printf("%zu\\n", sizeof(dsa_prefill_args));\n'
+                    + "".join(f'printf("%zu\\n", offsetof(dsa_prefill_args, {f}));\n'
+                              for f in fields) + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(dsa.PrefillArgs)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(dsa.PrefillArgs, f).offset == off, f
+
+
+INVALID, UNSUPPORTED = 1, 2
+P = ctypes.c_void_p
+A16 = ctypes.c_void_p(0x10000)   # aligned fake pointers: never dereferenced,
+A4 = ctypes.c_void_p(0x20004)    # validation fails before any HIP call
+
+
+def test_indexer_rejects_bad_arguments():
+    L = _lib()
+    f = L.dsa_indexer_logits
+    ok = dict(q=A16, qs=None, k=A16, ksc=A16, w=A16, ks=A16, ke=A16, out=A16, B=1, M=4, N=4,
+              H=64, D=128)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["q"], a["qs"], a["k"], a["ksc"], a["w"], a["ks"], a["ke"], a["out"], a["B"],
+                 a["M"], a["N"], a["H"], a["D"], None)
+
+    assert call(q=None) == INVALID
+    assert call(k=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(N=0) == INVALID
+    assert call(q=ctypes.c_void_p(0x10008)) == INVALID      # q not 16-byte aligned
+    assert call(ks=ctypes.c_void_p(0x10002)) == INVALID     # bounds not 4-byte aligned
+    assert call(N=1 << 31) == INVALID
+    assert call(H=5) == UNSUPPORTED
+    assert call(D=96) == UNSUPPORTED
+
+
+def test_topk_rejects_bad_arguments():
+    L = _lib()
+    f = L.dsa_topk
+    assert f(None, A16, A16, A16, 1, 4, 8, 2, None) == INVALID
+    assert f(A16, A16, A16, A16, 1, 4, 8, 0, None) == INVALID
+    assert f(A16, A16, A16, A16, 0, 4, 8, 2, None) == INVALID
+    assert f(A16, A16, A16, A16, 1, 4, 8, 4097, None) == UNSUPPORTED
+    assert f(A16, A16, ctypes.c_void_p(0x10001), A16, 1, 4, 8, 2, None) == INVALID
+
+
+def test_attention_rejects_bad_arguments():
+    L = _lib()
+    f = L.dsa_sparse_attn_fwd
+
+    def call(kv_dtype=0, kv_scale=None, Hq=128, Dqk=576, Dv=512, K=2048, q=A16, o=A16):
+        return f(q, A16, kv_dtype, kv_scale, None, A16, o, 1, 4, 8, Hq, Dqk, Dv, K, 0.0, None)
+
+    assert call(q=None) == INVALID
+    assert call(kv_dtype=1) == INVALID                # fp8 kv needs kv_scale
+    assert call(kv_dtype=0, kv_scale=A16) == INVALID  # bf16 kv must not have one
+    assert call(kv_dtype=7) == INVALID
+    assert call(Dv=600) == INVALID                    # Dv > Dqk
+    assert call(K=0) == INVALID
+    assert call(o=ctypes.c_void_p(0x10004)) == INVALID
+    assert call(Hq=24) == UNSUPPORTED
+    assert call(Dqk=128, Dv=128) == UNSUPPORTED
+    assert call(K=5000) == UNSUPPORTED
+    assert call(kv_dtype=1, kv_scale=A16, Dqk=64, Dv=64, Hq=16) == UNSUPPORTED
+
+
+def test_prefill_rejects_null_and_inconsistent():
+    L = _lib()
+    assert L.dsa_prefill(None, None) == INVALID
+    a = dsa.PrefillArgs()  # all zero
+    assert L.dsa_prefill(ctypes.byref(a), None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dsa, "_lib", None)
+    monkeypatch.setattr(dsa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        dsa.lib()

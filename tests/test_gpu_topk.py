@@ -1,0 +1,110 @@
+"""GPU parity: dsa_topk bit-exact against the oracle on the same logits."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_indexer_amd as dsa
+import oracle
+import workloads as W
+from gpu_util import dev, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(lg, ks, ke, K):
+    out = dsa.topk(dev(lg), dev(ks), dev(ke), K)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _compare(lg, ks, ke, K, rows=None, what=""):
+    lg = np.ascontiguousarray(lg, np.float32)
+    B, M, N = lg.shape
+    g = _run(lg, ks, ke, K).reshape(B * M, K)
+    flat = lg.reshape(B * M, N)
+    if rows is None:
+        ref = oracle.topk(flat, ks, ke, B, M, N, K)
+        got = g
+    else:
+        ref = oracle.topk(flat[rows], ks, ke, B, M, N, K, rows=rows)
+        got = g[rows]
+    bad = np.nonzero(~np.all(got == ref, axis=1))[0]
+    assert bad.size == 0, f"{what}: {bad.size} rows differ, first row {bad[0]}"
+
+
+def _dist(kind, shape, rng):
+    if kind == "normal":
+        return rng.standard_normal(shape).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(-4, 5, shape).astype(np.float32)
+    if kind == "special":
+        x = rng.standard_normal(shape).astype(np.float32)
+        m = rng.random(shape)
+        x[m < 0.1] = 0.0
+        x[(m >= 0.1) & (m < 0.2)] = -0.0
+        x[(m >= 0.2) & (m < 0.23)] = np.nan
+        x[(m >= 0.23) & (m < 0.26)] = -np.inf
+        x[(m >= 0.26) & (m < 0.28)] = np.inf
+        x[(m >= 0.28) & (m < 0.3)] = 1e-42  # denormal
+        return x
+    if kind == "narrow":  # one binade: the first radix digit sees a single bin
+        return (1.0 + rng.random(shape)).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special", "narrow"])
+@pytest.mark.parametrize("K", [1, 16, 100, 2048])
+def test_topk_small(kind, K):
+    rng = np.random.default_rng(K * 7 + len(kind))
+    B, M, N = 2, 40, 5000
+    lg = _dist(kind, (B, M, N), rng)
+    ks = rng.integers(-10, N, (B, M)).astype(np.int32)
+    ke = (ks + rng.integers(-5, 4500, (B, M))).astype(np.int32)
+    # pin the length edge cases: len = K-1, K, K+1, whole row
+    for i, ln in enumerate((K - 1, K, K + 1, N)):
+        ks[0, i] = 0
+        ke[0, i] = min(ln, N)
+    log(f"topk small {kind} K={K}")
+    _compare(lg, ks, ke, K, what=f"{kind}/K{K}")
+
+
+def test_topk_long_rows_streaming():
+    """Rows longer than the register-resident limit (8192 keys)."""
+    rng = np.random.default_rng(11)
+    B, M, N, K = 2, 3, 70000, 2048
+    lg = _dist("special", (B, M, N), rng)
+    ks = np.array([[0, 100, 60000], [0, 5, 0]], np.int32)
+    ke = np.array([[70000, 8300, 70000], [65536, 8197, 2048]], np.int32)
+    _compare(lg, ks, ke, K, what="long rows")
+    lg2 = _dist("ties", (B, M, N), rng)
+    _compare(lg2, ks, ke, 4096, what="long rows K=4096 ties")
+
+
+def test_topk_deterministic():
+    rng = np.random.default_rng(2)
+    lg = _dist("ties", (1, 64, 9000), rng)
+    ks = np.zeros((1, 64), np.int32)
+    ke = np.full((1, 64), 9000, np.int32)
+    a = _run(lg, ks, ke, 2048)
+    b = _run(lg, ks, ke, 2048)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,nrows", [("tiny_causal_256", None), ("prefill_4096", None),
+                                        ("varlen_4x8192", 1500), ("decode_b64", None),
+                                        ("prefill_8192_fp8kv", 1500)])
+def test_topk_workloads(name, nrows):
+    wl = W.WORKLOADS[name]
+    log(f"topk workload {name}")
+    lengths = None
+    if wl.windows == "decode":
+        lengths = W._gen(wl.seed, 0, 0).integers(wl.decode_min, wl.N, size=wl.B,
+                                                 endpoint=True).astype(np.int64)
+    ks, ke = W.bounds(wl, lengths=lengths)
+    lg = W.synthetic_logits(wl).numpy()
+    R = wl.B * wl.M
+    rows = None if nrows is None else sample_rows(R, nrows, seed=3,
+                                                  must=[0, R - 1, wl.K, wl.K - 1, wl.K + 1])
+    _compare(lg, ks, ke, wl.K, rows=rows, what=name)
+    lg_t = W.synthetic_logits(wl, ties=True).numpy()
+    _compare(lg_t, ks, ke, wl.K, rows=rows, what=name + "/ties")

@@ -188,3 +188,44 @@ def make_inputs(wl, parts=("indexer", "attn"), seed=None):
         del kv
         out["sink"] = torch.from_numpy(_normal(seed, 6, (wl.Hq,)))
     return out
+
+
+def synthetic_logits(wl, seed=None, ties=False):
+    """fp32 [B, M, N] stand-in scores for exercising top-k on its own:
+    N(0,1) draws (tensor id 7); with ties=True they are rounded to multiples
+    of 1/8 so that many keys share a value."""
+    import torch
+    seed = wl.seed if seed is None else seed
+    x = _normal(seed, 7, (wl.B, wl.M, wl.N))
+    if ties:
+        x = np.round(x * 8.0) / 8.0
+    return torch.from_numpy(x)
+
+
+def synthetic_topk(wl, ks, ke, seed=None, pad_frac=0.0):
+    """int32 [B, M, K] index lists shaped like a top-k result: a row whose
+    window [s, e) holds at most K keys lists all of them, otherwise K distinct
+    keys drawn uniformly from the window, ascending; -1 fills the rest.  With
+    pad_frac > 0 that fraction of rows also gets random -1 holes."""
+    import torch
+    seed = wl.seed if seed is None else seed
+    B, M, N, K = wl.B, wl.M, wl.N, wl.K
+    out = np.full((B * M, K), -1, np.int32)
+    s_all = np.clip(np.asarray(ks, np.int64).reshape(-1), 0, N)
+    e_all = np.maximum(np.clip(np.asarray(ke, np.int64).reshape(-1), 0, N), s_all)
+
+    def fill(r0):
+        rng = _gen(seed, 8, r0)
+        for r in range(r0, min(B * M, r0 + 256)):
+            s, e = int(s_all[r]), int(e_all[r])
+            if e - s <= K:
+                out[r, :e - s] = np.arange(s, e, dtype=np.int32)
+            else:
+                sel = rng.choice(e - s, size=K, replace=False)
+                out[r] = np.sort(sel).astype(np.int32) + s
+            if pad_frac > 0 and rng.random() < pad_frac:
+                holes = rng.random(K) < 0.3
+                out[r, holes] = -1
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, range(0, B * M, 256)))
+    return torch.from_numpy(out.reshape(B, M, K))
