@@ -1,0 +1,247 @@
+"""Benchmark of the DSA prefill hot path on one MI355X.
+
+One step = one pass of the whole path over the 4096-token causal prefill
+workload (batch 1; indexer 64 heads x 128 fp8; top-k 2048; sparse attention
+128 heads over 576-wide bf16 latent KV, 512-wide output): dsa_indexer_logits
+-> dsa_topk -> dsa_sparse_attn_fwd on one stream (exactly the launches that
+dsa_prefill makes), with inputs resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is tokens/s of the whole step.  `roofline`
+describes the dominant kernel (sparse attention): algorithmic bf16 flops per
+launch over its average duration from HIP events on the launch stream,
+against the 2.5 PFLOP/s dense bf16 MFMA peak.  `cpu_baseline` times the CPU
+oracle (indexer -> top-k -> attention) on a bounded sample of rows.
+
+    python bench.py [--steps 20] [--warmup 5] [--gpus 1] [--no-cpu]
+    python bench.py --copy-calibration     # plain 1 GiB copy, for counter scaling
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA prefill tokens/s (indexer+top-k+sparse attn) at seq 4096; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_prefill_4096_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "fp8_indexer_amd", "csrc", "sparse_attn.hip")
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work_counts(wl, ks, ke):
+    """Algorithmic work of each stage (valid pairs only)."""
+    import numpy as np
+    s = np.clip(ks.reshape(-1).astype(np.int64), 0, wl.N)
+    e = np.maximum(np.clip(ke.reshape(-1).astype(np.int64), 0, wl.N), s)
+    ln = e - s
+    p_idx = int(ln.sum())
+    p_att = int(np.minimum(ln, wl.K).sum())
+    rows = wl.B * wl.M
+    idx_flops = 2.0 * wl.H * wl.D * p_idx
+    idx_bytes = (rows * wl.H * wl.D + wl.B * wl.N * (wl.D + 4) + 8 * rows * wl.H + 4 * p_idx)
+    topk_bytes = 4.0 * ln[ln > wl.K].sum() + 4.0 * wl.K * rows
+    att_flops = 2.0 * wl.Hq * (wl.Dqk + wl.Dv) * p_att
+    return dict(p_idx=p_idx, p_att=p_att, idx_flops=idx_flops, idx_bytes=float(idx_bytes),
+                topk_bytes=float(topk_bytes), att_flops=att_flops)
+
+
+def attn_src_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(launches_per_step=1):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary; None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != attn_src_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, x, budget_s):
+    """The oracle on a bounded sample of rows, evenly spaced over the
+    sequence so that the average window length matches the workload."""
+    import numpy as np
+    import oracle
+    R = wl.B * wl.M
+
+    def run(rows):
+        t0 = time.perf_counter()
+        lg = oracle.indexer_logits(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"],
+                                   x["ks"], x["ke"], rows=rows)
+        ti = oracle.topk(lg, x["ks"], x["ke"], wl.B, wl.M, wl.N, wl.K, rows=rows)
+        full = np.full((R, wl.K), -1, np.int32)
+        full[rows] = ti
+        oracle.sparse_attn(x["q"], x["kv"], x["sink"], full.reshape(wl.B, wl.M, wl.K),
+                           wl.sm_scale, wl.Dv, kv_scale=x["kv_scale"], rows=rows)
+        return time.perf_counter() - t0
+
+    n = 16
+    rows = np.linspace(0, R - 1, n).round().astype(np.int64)
+    dt = run(rows)
+    n2 = int(min(R, max(n, n * (budget_s / max(dt, 1e-3)))))
+    if n2 > n:
+        rows = np.unique(np.linspace(0, R - 1, n2).round().astype(np.int64))
+        dt = run(rows)
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {R} query rows, evenly spaced over the 4096-token "
+                      f"causal prefill (indexer -> top-k -> attention, fp64 C oracle), "
+                      f"{dt:.1f} s"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the work shards by query rows; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import fp8_indexer_amd as dsa
+    import workloads as W
+
+    wl = W.WORKLOADS["prefill_4096"]
+    eprint(f"[bench] generating inputs for {wl.name}")
+    x = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    g = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else
+             (v.to(dev) if isinstance(v, torch.Tensor) else v)) for k, v in x.items()}
+    B, M, N = wl.B, wl.M, wl.N
+    logits = torch.empty((B, M, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, M, wl.K), dtype=torch.int32, device=dev)
+    o = torch.empty((B, M, wl.Hq, wl.Dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.indexer_logits(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"],
+                           g["ke"], logits=logits)
+        if ev:
+            ev[1].record(stream)
+        dsa.topk(logits, g["ks"], g["ke"], wl.K, out=idx)
+        if ev:
+            ev[2].record(stream)
+        dsa.sparse_attn_fwd(g["q"], g["kv"], g["sink"], idx, wl.sm_scale, wl.Dv, out=o)
+        if ev:
+            ev[3].record(stream)
+
+    eprint(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    eprint(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    ms_idx, ms_topk, ms_att = st.mean(axis=0)
+
+    # whole-path entry point, same work, as a cross-check of the step time
+    for _ in range(2):
+        dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
+                    wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
+                    logits=logits, topk_idxs=idx, out=o)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(args.steps):
+        dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
+                    wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
+                    logits=logits, topk_idxs=idx, out=o)
+    torch.cuda.synchronize()
+    ms_prefill = (time.perf_counter() - tp0) * 1e3 / args.steps
+
+    wc = work_counts(wl, x["ks"], x["ke"])
+    tokens = B * M
+    att_tflops = wc["att_flops"] / (ms_att * 1e-3) / 1e12
+    idx_tflops = wc["idx_flops"] / (ms_idx * 1e-3) / 1e12
+    topk_gbs = wc["topk_bytes"] / (ms_topk * 1e-3) / 1e9
+    roof_s = (wc["idx_flops"] / (PEAK_FP8_TFLOPS * 1e12) + wc["topk_bytes"] / (PEAK_HBM_GBS * 1e9)
+              + wc["att_flops"] / (PEAK_BF16_TFLOPS * 1e12))
+    traffic = load_traffic()
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "seq_len": M, "index_heads": wl.H,
+                   "index_dim": wl.D, "topk": wl.K, "heads": wl.Hq, "dqk": wl.Dqk, "dv": wl.Dv,
+                   "kv": "bf16", "windows": "causal"},
+        "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel",
+                     "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": att_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "stages": {
+            "indexer": {"ms": ms_idx, "tflops": idx_tflops,
+                        "frac_fp8_peak": idx_tflops / PEAK_FP8_TFLOPS},
+            "topk": {"ms": ms_topk, "gbs": topk_gbs, "frac_hbm": topk_gbs / PEAK_HBM_GBS,
+                     "rows_per_s": tokens / (ms_topk * 1e-3)},
+            "attention": {"ms": ms_att, "tflops": att_tflops,
+                          "frac_bf16_peak": att_tflops / PEAK_BF16_TFLOPS},
+            "prefill_entry_ms": ms_prefill,
+            "e2e_roofline_ms": roof_s * 1e3,
+            "e2e_frac_of_roofline": roof_s * 1e3 / ms_step,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        eprint("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
