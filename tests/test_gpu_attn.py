@@ -110,3 +110,33 @@ def test_attn_workloads(name):
         og = og[torch.from_numpy(rows).to(og.device)]
     mx, mn = check_attn(og, ref, name)
     log(f"  max|d| {mx:.3g} mean|d| {mn:.3g}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("where", ["middle", "last", "first"])
+def test_attn_reference_restart(fp8, where):
+    """A score far above every score of the first tile (the kernel's fixed
+    softmax reference) forces the max-only pre-pass and the second pass."""
+    B, M, N, K = 1, 2, 600, 256
+    wl = W.Workload("r", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, kv_fp8=fp8,
+                    seed=6)
+    x = W.make_inputs(wl, parts=("attn",))
+    big = {"middle": 300, "last": 599, "first": 3}[where]
+    qv = torch.ones((B, M, wl.Hq, wl.Dqk), dtype=torch.float32) * 0.5
+    qv[..., ::2] = 1.0
+    x["q"] = qv.to(torch.bfloat16)
+    kvf = torch.from_numpy(np.random.default_rng(1).standard_normal((B, N, wl.Dqk))
+                           .astype(np.float32))
+    kvf[0, big] = 4.0          # q.k/24 = 72 (natural units) above the others
+    kvf[0, big, :8] = -3.0
+    if fp8:
+        x["kv"], x["kv_scale"] = W.quantize_e4m3fn_rows(kvf.numpy())
+    else:
+        x["kv"] = kvf.to(torch.bfloat16)
+    idx = np.tile(np.arange(0, 2 * K, 2, dtype=np.int32), (B, M, 1))  # rows 0,2,..,510
+    idx[0, 0, K // 2] = big
+    idx[0, 1, 0 if where == "first" else K - 1] = big
+    o = _run(x, idx, wl)
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
+                             kv_scale=x["kv_scale"])
+    check_attn(o, ref, f"restart/{where}")
