@@ -33,6 +33,14 @@ constexpr int kRowsPerWave = 128;               // (token, head) rows per wave
 constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
 constexpr int kKT = 64;                         // keys per LDS tile
 constexpr int kXcds = 8;
+#ifndef DSA_IDX_MIN_CHUNK
+#define DSA_IDX_MIN_CHUNK 512
+#endif
+#ifndef DSA_IDX_MAX_CHUNKS
+#define DSA_IDX_MAX_CHUNKS 16
+#endif
+constexpr int kMinChunk = DSA_IDX_MIN_CHUNK;    // keys (tuning knob)
+constexpr int kMaxChunks = DSA_IDX_MAX_CHUNKS;  // chunks per key axis (tuning knob)
 
 template <int H, int D>
 struct IdxCfg {
@@ -45,7 +53,43 @@ struct IdxCfg {
   static constexpr int TILE_BYTES = kKT * D;
   static constexpr int CHUNKS = kKT * CPR;
   static constexpr int CPT = (CHUNKS + kIdxThreads - 1) / kIdxThreads;
+  // Row placement: C element (row tile rt, lane group g, i) holds the row
+  // with group-major index L = 32*g + 4*rt + i, i.e. token L / H, head L % H.
+  // A lane group then holds whole tokens (H <= 32: TPL tokens per lane, no
+  // cross-lane sum) or 1/GPT of one token (H = 64, 128: GPT lane groups are
+  // summed with 1 or 2 lane swaps).
+  static constexpr int TPL = H < 32 ? 32 / H : 1;  // tokens per lane
+  static constexpr int GPT = H > 32 ? H / 32 : 1;  // lane groups per token
 };
+
+// Sum of v over the lanes l and l^16 (S = 16) or l and l^32 (S = 32), using
+// gfx950's row-swap permutes (no LDS round trip).  With both inputs equal,
+// the two results are the two halves of the butterfly; the empty asm keeps
+// the compiler from folding their sum as if they were the same value (it
+// emits r0 + r0 without it).
+template <int S>
+__device__ __forceinline__ float lane_swap_sum(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  unsigned a, c;
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = r[0];
+    c = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = r[0];
+    c = r[1];
+  }
+  asm volatile("" : "+v"(a), "+v"(c));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, c);
+}
+
+// max(x, 0) for a non-NaN float as one integer max on its bits (negative
+// floats are negative integers; -0 becomes +0), without the NaN-quieting
+// canonicalisation that fmaxf costs.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
 
 // Byte offset of logical 16-byte chunk c of key row kk inside an LDS tile:
 // chunks are XOR-swizzled by the row so that 16 lanes reading the same
@@ -121,8 +165,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   float weff[kRT][4];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const int row = rt * 16 + col;
-    const int t = tw0 + row / H, h = row % H;
+    // A row col of tile rt is C row (g', i') = (col / 4, col % 4)
+    const int L = 32 * (col >> 2) + 4 * rt + (col & 3);
+    const int t = tw0 + L / H, h = L % H;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const int d0 = s * 128 + g * 32;
@@ -136,8 +181,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r2 = rt * 16 + g * 4 + i;
-      const int t2 = tw0 + r2 / H, h2 = r2 % H;
+      const int L2 = 32 * g + 4 * rt + i;
+      const int t2 = tw0 + L2 / H, h2 = L2 % H;
       float we = 0.f;
       if (t2 < M) {
         const size_t o = (size_t)(b * M + t2) * H + h2;
@@ -146,27 +191,39 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       weff[rt][i] = we;
     }
   }
-  int ws[C::TW], we_[C::TW];
+  // windows of the wave (for tile skipping) and of this lane's tokens
+  // (token of slot j: (32*g)/H + j), clipped to the chunk so that
+  // zero-filled keys are never written
   int wmin = N, wmax = 0;
-#pragma unroll
   for (int tl = 0; tl < C::TW; ++tl) {
     const int t = tw0 + tl;
+    if (t < M) {
+      const int r = b * M + t;
+      const int s = max(clampi(ks[r], 0, N), c0);
+      const int e = min(clampi(ke[r], 0, N), c1);
+      if (e > s) {
+        wmin = min(wmin, s);
+        wmax = max(wmax, e);
+      }
+    }
+  }
+  int ls[C::TPL], le[C::TPL];
+  float* orow[C::TPL];
+#pragma unroll
+  for (int j = 0; j < C::TPL; ++j) {
+    const int t = tw0 + (32 * g) / H + j;
     int s = 0, e = 0;
     if (t < M) {
       const int r = b * M + t;
       s = clampi(ks[r], 0, N);
       e = clampi(ke[r], s, N);
     }
-    // restrict to this chunk so that zero-filled keys are never written
-    s = max(s, c0);
-    e = min(e, c1);
-    ws[tl] = s;
-    we_[tl] = e;
-    if (e > s) {
-      wmin = min(wmin, s);
-      wmax = max(wmax, e);
-    }
+    ls[j] = max(s, c0);
+    le[j] = min(e, c1);
+    orow[j] = logits + (size_t)(b * M + min(t, M - 1)) * N;
   }
+  // a lane stores the sums of its tokens if it is the first of their groups
+  const bool store_lane = (g % C::GPT) == 0;
 
   // ---- K tile staging -----------------------------------------------------
   const int ntiles = (c1 - c0 + kKT - 1) / kKT;
@@ -210,65 +267,65 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     if (tile + 1 < ntiles) gload(tile + 1);
     // skip waves whose tokens do not see this tile
     if (wmax > kb && wmin < kb + kKT) {
-#pragma unroll 1
-      for (int n = 0; n < kKT / 16; ++n) {
+      // 16-key sub-tiles, software pipelined (128-deep keys): the MFMAs of
+      // sub-tile n+1 are issued before the epilogue of sub-tile n
+      constexpr int NB = C::KS == 1 ? 2 : 1;
+      f32x4 acc[NB][kRT];
+      auto mm = [&](int n, f32x4* a) {
         const int kk = n * 16 + col;
-        f32x4 acc[kRT];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < kRT; ++rt) a[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
           i32x8 bf = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (s * 128 + g * 32 < D) {
+          if (D % 128 == 0 || s * 128 + g * 32 < D) {
             const int c = s * 8 + g * 2;
             const i32x4 lo = *reinterpret_cast<const i32x4*>(&sK[buf][tile_off<D>(kk, c)]);
             const i32x4 hi = *reinterpret_cast<const i32x4*>(&sK[buf][tile_off<D>(kk, c + 1)]);
             bf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma_f8_16x16x128(qf[rt][s], bf, acc[rt]);
+          for (int rt = 0; rt < kRT; ++rt) a[rt] = mfma_f8_16x16x128(qf[rt][s], bf, a[rt]);
         }
-        // epilogue: relu * weight, sum over heads, * k_scale, masked store
+      };
+      // epilogue: relu * weight, sum over heads, * k_scale, masked store
+      auto epi = [&](int n, const f32x4* a) {
+        const int kk = n * 16 + col;
         const float ksc = sKs[buf][kk];
         const int key = kb + kk;
-        float* out_col = logits + (size_t)key;
-        if constexpr (H >= 16) {
-          constexpr int TPT = H / 16;  // MFMA tiles per token
+        // 4 independent partial sums per token (short dependency chains)
+        float part[C::TPL][4];
 #pragma unroll
-          for (int tl = 0; tl < C::TW; ++tl) {
-            float sum = 0.f;
+        for (int j = 0; j < C::TPL; ++j)
 #pragma unroll
-            for (int rr = 0; rr < TPT; ++rr) {
-              const int rt = tl * TPT + rr;
+          for (int i = 0; i < 4; ++i) part[j][i] = 0.f;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
-            }
-            sum += wave_xor(sum, 16);
-            sum += wave_xor(sum, 32);
-            if ((tl & 3) == g && key >= ws[tl] && key < we_[tl])
-              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
-          }
-        } else if constexpr (H == 8) {
+        for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            float sum = 0.f;
+          for (int i = 0; i < 4; ++i)
+            part[(4 * rt + i) / (32 / C::TPL)][i] =
+                fmaf(relu(a[rt][i]), weff[rt][i], part[(4 * rt + i) / (32 / C::TPL)][i]);
+        float sum[C::TPL];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
-            sum += wave_xor(sum, 16);
-            const int tl = rt * 2 + (g >> 1);
-            if ((g & 1) == 0 && key >= ws[tl] && key < we_[tl])
-              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
-          }
-        } else {  // H == 4: one token per lane group
+        for (int j = 0; j < C::TPL; ++j) sum[j] = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
+        if constexpr (C::GPT >= 2) sum[0] = lane_swap_sum<16>(sum[0]);
+        if constexpr (C::GPT >= 4) sum[0] = lane_swap_sum<32>(sum[0]);
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            float sum = 0.f;
+        for (int j = 0; j < C::TPL; ++j)
+          if (store_lane && key >= ls[j] && key < le[j]) orow[j][key] = sum[j] * ksc;
+      };
+      if constexpr (NB == 2) {
+        mm(0, acc[0]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += fmaxf(acc[rt][i], 0.f) * weff[rt][i];
-            const int tl = rt * 4 + g;
-            if (key >= ws[tl] && key < we_[tl])
-              out_col[(size_t)(b * M + tw0 + tl) * N] = sum * ksc;
-          }
+        for (int n = 0; n < kKT / 16; ++n) {
+          if (n + 1 < kKT / 16) mm(n + 1, acc[(n + 1) & 1]);
+          epi(n, acc[n & 1]);
+        }
+      } else {
+#pragma unroll 1
+        for (int n = 0; n < kKT / 16; ++n) {
+          mm(n, acc[0]);
+          epi(n, acc[0]);
         }
       }
     }
@@ -282,9 +339,10 @@ hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
   using C = IdxCfg<H, D>;
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
   const int n_tblocks_pad = (n_tblocks + kXcds - 1) / kXcds * kXcds;
-  // Key chunk: at least 512 keys, at most 16 chunks over the key axis.
-  int chunk_keys = (int)((a.N + 15) / 16);
-  chunk_keys = max(512, (chunk_keys + kKT - 1) / kKT * kKT);
+  // Key chunk: at least kMinChunk keys, at most kMaxChunks chunks over the
+  // key axis (a chunk reloads its block's q).
+  int chunk_keys = (int)((a.N + kMaxChunks - 1) / kMaxChunks);
+  chunk_keys = max(kMinChunk, (chunk_keys + kKT - 1) / kKT * kKT);
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
   const long long blocks = (long long)a.B * n_tblocks_pad * n_chunks;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
