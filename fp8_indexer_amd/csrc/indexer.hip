@@ -27,20 +27,19 @@
 namespace dsa {
 namespace {
 
-constexpr int kIdxWaves = 8;
-constexpr int kIdxThreads = kIdxWaves * kWave;  // 512
+// Waves per workgroup (tuning knob): 4 lets two workgroups share a CU, so
+// one's start-up (q loads, window reduction, first key tile) overlaps the
+// other's tiles; 8 shares each key tile among more waves.
+#ifndef DSA_IDX_WAVES
+#define DSA_IDX_WAVES 4
+#endif
+constexpr int kIdxWaves = DSA_IDX_WAVES;
+constexpr int kIdxThreads = kIdxWaves * kWave;
 constexpr int kRowsPerWave = 128;               // (token, head) rows per wave
 constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
 constexpr int kKT = 64;                         // keys per LDS tile
 constexpr int kXcds = 8;
-#ifndef DSA_IDX_MIN_CHUNK
-#define DSA_IDX_MIN_CHUNK 512
-#endif
-#ifndef DSA_IDX_MAX_CHUNKS
-#define DSA_IDX_MAX_CHUNKS 16
-#endif
-constexpr int kMinChunk = DSA_IDX_MIN_CHUNK;    // keys (tuning knob)
-constexpr int kMaxChunks = DSA_IDX_MAX_CHUNKS;  // chunks per key axis (tuning knob)
+constexpr int kMinChunk = 512;  // keys per chunk, at least
 
 template <int H, int D>
 struct IdxCfg {
@@ -82,6 +81,30 @@ __device__ __forceinline__ float lane_swap_sum(float v) {
   }
   asm volatile("" : "+v"(a), "+v"(c));
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, c);
+}
+
+// Minimum over the 64 lanes of a wave: DPP within each 16-lane row, then
+// the two row-swap permutes (no LDS round trip).
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  unsigned a, c;
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    a = r[0];
+    c = r[1];
+  }
+  asm volatile("" : "+v"(a), "+v"(c));  // see lane_swap_sum
+  v = min((int)a, (int)c);
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    a = r[0];
+    c = r[1];
+  }
+  asm volatile("" : "+v"(a), "+v"(c));
+  return min((int)a, (int)c);
 }
 
 // max(x, 0) for a non-NaN float as one integer max on its bits (negative
@@ -126,40 +149,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   if (tb < 0 || tb >= n_tblocks) return;
   const int t0 = tb * C::TB;
 
-  // ---- window union of the block: [kmin, kmax) ---------------------------
-  int smin = N, emax = 0;
-  for (int i = tid; i < C::TB; i += kIdxThreads) {
-    const int t = t0 + i;
-    if (t < M) {
-      const int r = b * M + t;
-      const int s = clampi(ks[r], 0, N);
-      const int e = clampi(ke[r], s, N);
-      if (e > s) {
-        smin = min(smin, s);
-        emax = max(emax, e);
-      }
-    }
-  }
-  for (int m = 32; m >= 1; m >>= 1) {
-    smin = min(smin, __shfl_xor(smin, m, kWave));
-    emax = max(emax, __shfl_xor(emax, m, kWave));
-  }
-  if (lane == 0) {
-    sRed[0][wave] = smin;
-    sRed[1][wave] = emax;
-  }
-  __syncthreads();
-  int kmin = sRed[0][0], kmax = sRed[1][0];
-#pragma unroll
-  for (int i = 1; i < kIdxWaves; ++i) {
-    kmin = min(kmin, sRed[0][i]);
-    kmax = max(kmax, sRed[1][i]);
-  }
-  const int c0 = kmin + chunk * chunk_keys;
-  if (kmin >= kmax || c0 >= kmax) return;  // uniform across the workgroup
-  const int c1 = min(kmax, c0 + chunk_keys);
-
-  // ---- this wave's tokens: q fragments, effective weights, windows -------
+  // ---- this wave's tokens: q fragments and effective weights (issued
+  // before the window reduction, which they do not depend on) ------------
   const int tw0 = t0 + wave * C::TW;
   i32x8 qf[kRT][C::KS];
   float weff[kRT][4];
@@ -191,6 +182,37 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       weff[rt][i] = we;
     }
   }
+  // ---- window union of the block: [kmin, kmax) ---------------------------
+  int smin = N, emax = 0;
+  for (int i = tid; i < C::TB; i += kIdxThreads) {
+    const int t = t0 + i;
+    if (t < M) {
+      const int r = b * M + t;
+      const int s = clampi(ks[r], 0, N);
+      const int e = clampi(ke[r], s, N);
+      if (e > s) {
+        smin = min(smin, s);
+        emax = max(emax, e);
+      }
+    }
+  }
+  smin = wave_min(smin);
+  emax = -wave_min(-emax);
+  if (lane == 0) {
+    sRed[0][wave] = smin;
+    sRed[1][wave] = emax;
+  }
+  __syncthreads();
+  int kmin = sRed[0][0], kmax = sRed[1][0];
+#pragma unroll
+  for (int i = 1; i < kIdxWaves; ++i) {
+    kmin = min(kmin, sRed[0][i]);
+    kmax = max(kmax, sRed[1][i]);
+  }
+  const int c0 = kmin + chunk * chunk_keys;
+  if (kmin >= kmax || c0 >= kmax) return;  // uniform across the workgroup
+  const int c1 = min(kmax, c0 + chunk_keys);
+
   // windows of the wave (for tile skipping) and of this lane's tokens
   // (token of slot j: (32*g)/H + j), clipped to the chunk so that
   // zero-filled keys are never written
@@ -339,10 +361,23 @@ hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
   using C = IdxCfg<H, D>;
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
   const int n_tblocks_pad = (n_tblocks + kXcds - 1) / kXcds * kXcds;
-  // Key chunk: at least kMinChunk keys, at most kMaxChunks chunks over the
-  // key axis (a chunk reloads its block's q).
-  int chunk_keys = (int)((a.N + kMaxChunks - 1) / kMaxChunks);
-  chunk_keys = max(kMinChunk, (chunk_keys + kKT - 1) / kKT * kKT);
+  // Key chunks: a chunk reloads its token block's q, so blocks are split
+  // only as far as needed to give every workgroup slot of the device an item
+  // (decode-like inputs with few token blocks), with chunks of >= 512 keys.
+  int cus = 256;
+  {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  const long long slots = (long long)cus * (8 / kIdxWaves);  // 2 waves per SIMD, 4 SIMDs
+  const long long tblocks = (long long)a.B * n_tblocks;
+  const long long max_chunks = (a.N + kMinChunk - 1) / kMinChunk;
+  const long long want = (slots + tblocks - 1) / tblocks;
+  const int n_chunks0 = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
+  int chunk_keys = (int)((a.N + n_chunks0 - 1) / n_chunks0);
+  chunk_keys = (chunk_keys + kKT - 1) / kKT * kKT;
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
   const long long blocks = (long long)a.B * n_tblocks_pad * n_chunks;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
