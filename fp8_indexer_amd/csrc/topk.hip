@@ -16,9 +16,12 @@
 // (K - #above) keys == tau, at their ascending output slot.  No atomics touch
 // the output, so it is deterministic.
 //
-// One 512-thread workgroup per row.  Rows up to 8192 keys are read from HBM
-// once and kept in VGPRs (16 keys per lane); longer rows are re-read from L2
-// on each pass.  Rows with len <= K only write s..e-1 and -1 padding.
+// Rows of up to 8192 keys (N <= 8192): one 256-thread workgroup per row,
+// each wave holding a contiguous quarter of the row in VGPRs (digits of 11,
+// 11 and 10 bits, a shared LDS histogram, wave-level scans).  Longer rows:
+// one 512-thread workgroup per row, 16 keys per lane in VGPRs up to 8192
+// keys and re-read from L2 on each pass beyond (digits 12, 10, 10).  Rows
+// with len <= K only write s..e-1 and -1 padding.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -184,11 +187,167 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   }
 }
 
+
+// ---- four waves per row ----------------------------------------------------
+// For rows of at most 256*KR keys: wave w holds the contiguous segment
+// [w*64*KR, (w+1)*64*KR) of the row in VGPRs (lane l: keys w*64*KR + 64c +
+// l), the histogram is shared in LDS, and digits are 11, 11 and 10 bits with
+// three barriers per digit.  Emission: each wave counts its keys above tau
+// and equal to tau, one barrier exchanges the counts, then every wave writes
+// its segment in index order with ballots.  Same selection rule as above.
+#ifndef DSA_TOPK_ROW_WAVES
+#define DSA_TOPK_ROW_WAVES 4
+#endif
+constexpr int kRowWaves = DSA_TOPK_ROW_WAVES;  // waves per row (tuning knob)
+constexpr int kRowThreads = kRowWaves * kWave;
+
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+template <int KR>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
+                                                               const int* __restrict__ ks,
+                                                               const int* __restrict__ ke,
+                                                               int* __restrict__ out, int N, int K) {
+  constexpr int SEG = kWave * KR;
+  __shared__ __align__(16) uint32_t hist[2048];
+  __shared__ int sRed[kRowWaves];
+  __shared__ int sSel[2];
+  __shared__ int sCnt[2][kRowWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t r = blockIdx.x;
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  const int len = e - s;
+  int* o = out + r * (size_t)K;
+  if (len <= K) {
+    for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
+    return;
+  }
+  const float* row = logits + r * (size_t)N + s;
+  const int base = wave * SEG;
+  uint32_t keys[KR];
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    const int i = base + c * kWave + lane;
+    keys[c] = i < len ? order_key(row[i]) : 0u;
+  }
+
+  uint32_t prefix = 0;
+  int krem = K, above_total = 0;
+#pragma unroll
+  for (int round = 0; round < 3; ++round) {
+    const int bits = round < 2 ? 11 : 10;
+    const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
+    const int nb = 1 << bits;
+    const int bpt = nb / kRowThreads;  // bins per thread
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < KR; ++c) {
+      if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
+      const int i = base + c * kWave + lane;
+      const uint32_t u = keys[c];
+      if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
+        atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    int tsum = 0;
+    for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
+    const int incl_w = wave_incl_scan(tsum);
+    if (lane == 63) sRed[wave] = incl_w;
+    __syncthreads();
+    int pre = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const int t = sRed[w];
+      pre += w < wave ? t : 0;
+      total += t;
+    }
+    int above = total - (pre + incl_w);  // keys in bins of higher threads
+    if (above < krem && krem <= above + tsum) {  // exactly one thread
+      for (int j = bpt - 1; j >= 0; --j) {
+        const int c = (int)hist[tid * bpt + j];
+        if (above < krem && krem <= above + c) {
+          sSel[0] = tid * bpt + j;
+          sSel[1] = above;
+        }
+        above += c;
+      }
+    }
+    __syncthreads();
+    const int bin = sSel[0], ab = sSel[1];
+    prefix = (prefix << bits) | (uint32_t)bin;
+    krem -= ab;
+    above_total += ab;
+  }
+  const uint32_t tau = prefix;
+  const int n_eq = K - above_total;
+
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    if (base + c * kWave >= len) break;
+    const int i = base + c * kWave + lane;
+    gtc += (int)__popcll(__ballot(i < len && keys[c] > tau));
+    eqc += (int)__popcll(__ballot(i < len && keys[c] == tau));
+  }
+  if (lane == 0) {
+    sCnt[0][wave] = gtc;
+    sCnt[1][wave] = eqc;
+  }
+  __syncthreads();
+  int gt_base = 0, eq_base = 0;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    gt_base += w < wave ? sCnt[0][w] : 0;
+    eq_base += w < wave ? sCnt[1][w] : 0;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_run = eq_base, sel_run = gt_base + min(eq_base, n_eq);
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    if (base + c * kWave >= len) break;
+    const int i = base + c * kWave + lane;
+    const uint32_t u = keys[c];
+    const bool valid = i < len;
+    const bool gt = valid && u > tau;
+    const bool eq = valid && u == tau;
+    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+    const int eq_before = __popcll(meq & lt_mask);
+    const int eq_left = max(0, n_eq - eq_run);
+    const bool eq_sel = eq && eq_before < eq_left;
+    const int pos = sel_run + __popcll(mgt & lt_mask) + min(eq_before, eq_left);
+    if ((gt || eq_sel) && pos < K) o[pos] = s + i;
+    sel_run += __popcll(mgt) + min((int)__popcll(meq), eq_left);
+    eq_run += __popcll(meq);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const long long rows = a.B * a.M;
   if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  // rows of up to 8192 keys: kRowWaves waves per row, keys in VGPRs
+  if (a.N <= kRowThreads * (4096 / kRowThreads)) {
+    hipLaunchKernelGGL(topk_row_kernel<4096 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
+                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+    return hipGetLastError();
+  }
+  if (a.N <= kRowThreads * (8192 / kRowThreads)) {
+    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
+                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a.logits,
                      a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
   return hipGetLastError();
