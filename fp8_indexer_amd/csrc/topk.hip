@@ -4,8 +4,9 @@
 // order-preserving unsigned keys; a histogram of the leading key bits and a
 // cumulative sum locate the bin that holds the K-th largest value; only that
 // bin is refined on the next bits, so the exact threshold is found without
-// sorting the row.  Here the 32-bit key is resolved in three MSD rounds of
-// 12, 10 and 10 bits with LDS histograms (4096 / 1024 bins).
+// sorting the row.  Here the 32-bit key is resolved in three MSD rounds
+// (11, 11, 10 bits, or 12, 10, 10 for rows beyond 8192 keys) with LDS
+// histograms.
 //
 // Selection rule (this library's contract): the K keys of [s, e) first in
 // (value descending, index ascending) order, with -0 == +0 and NaN ranked as
