@@ -8,11 +8,13 @@ dsa_prefill makes), with inputs resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is tokens/s of the whole step.  `roofline`
 describes the dominant kernel (sparse attention): algorithmic bf16 flops per
-launch over its average duration from HIP events on the launch stream,
-against the 2.5 PFLOP/s dense bf16 MFMA peak.  `cpu_baseline` times the CPU
+launch over its median duration from HIP events on the launch stream,
+against the 2.5 PFLOP/s dense bf16 MFMA peak.  `stages` also gives each
+stage timed with L2 and the MALL flushed before every step, and the
+dsa_prefill entry point warm and flushed.  `cpu_baseline` times the CPU
 oracle (indexer -> top-k -> attention) on a bounded sample of rows.
 
-    python bench.py [--steps 20] [--warmup 5] [--gpus 1] [--no-cpu]
+    python bench.py [--steps 20] [--warmup 5] [--gpus 1] [--no-cpu] [--flush-reps 10]
     python bench.py --copy-calibration     # plain 1 GiB copy, for counter scaling
 """
 import argparse
@@ -124,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--flush-reps", type=int, default=10,
+                    help="steps timed with L2/MALL flushed before each (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -181,7 +185,33 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
-    ms_idx, ms_topk, ms_att = st.mean(axis=0)
+    ms_idx, ms_topk, ms_att = np.median(st, axis=0)
+
+    # the same stages with L2 and the 256 MB MALL flushed before each step
+    # (a 512 MB write), so no stage reads its input from the previous one's
+    # cache footprint
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fl = []
+    for _ in range(args.flush_reps):
+        flush_buf.fill_(1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        fl.append([ev[j].elapsed_time(ev[j + 1]) for j in range(3)])
+    flushed = np.median(np.array(fl), axis=0) if fl else [float("nan")] * 3
+    pf = []
+    for _ in range(args.flush_reps):
+        flush_buf.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
+                    wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
+                    logits=logits, topk_idxs=idx, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pf.append(e0.elapsed_time(e1))
+    ms_prefill_flushed = float(np.median(pf)) if pf else float("nan")
+    del flush_buf
 
     # whole-path entry point, same work, as a cross-check of the step time
     for _ in range(2):
@@ -232,6 +262,10 @@ def main():
             "attention": {"ms": ms_att, "tflops": att_tflops,
                           "frac_bf16_peak": att_tflops / PEAK_BF16_TFLOPS},
             "prefill_entry_ms": ms_prefill,
+            "prefill_entry_flushed_ms": ms_prefill_flushed,
+            "flushed_ms": {"indexer": float(flushed[0]), "topk": float(flushed[1]),
+                           "attention": float(flushed[2]), "reps": args.flush_reps},
+            "timing": "stage ms: median over the timed steps of HIP events on the launch stream",
             "e2e_roofline_ms": roof_s * 1e3,
             "e2e_frac_of_roofline": roof_s * 1e3 / ms_step,
         },
