@@ -136,6 +136,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   __shared__ __align__(16) uint16_t sKV[2][C::TILE];
   __shared__ int sIdx[kMaxK];           // sanitised indices (-1 = invalid), padded
   __shared__ int sList[kMaxK / kBI];    // tiles with a valid index, ascending
+  __shared__ int sFirst[kMaxK / kBI];   // first valid index of each tile, or -1
   __shared__ float sSc[2][kBI];         // FP8: per-row scales of a tile
   __shared__ int sNvt;
   __shared__ int sFlag[2];  // a score above its reference + slack, by tile parity
@@ -163,10 +164,15 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     int base = 0;
     for (int t0 = 0; t0 < ntiles; t0 += kWave) {
       const int t = t0 + lane;
-      bool f = false;
+      int first = -1;
       if (t < ntiles) {
-        for (int r = 0; r < kBI; ++r) f = f || sIdx[t * kBI + r] >= 0;
+        for (int r = kBI - 1; r >= 0; --r) {
+          const int v = sIdx[t * kBI + r];
+          first = v >= 0 ? v : first;
+        }
+        sFirst[t] = first;
       }
+      const bool f = first >= 0;
       const uint64_t m = __ballot(f);
       if (f) sList[base + __popcll(m & lt)] = t;
       base += __popcll(m);
@@ -201,6 +207,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   }
   __syncthreads();
   const int nvt = sNvt;
+  // invalid slots of tiles with a valid index -> -1 - (first valid index)
+  for (int p = tid; p < ntiles * kBI; p += C::THREADS) {
+    const int first = sFirst[p / kBI];
+    if (sIdx[p] < 0 && first >= 0) sIdx[p] = -1 - first;
+  }
+  __syncthreads();
 
   // ---- tile staging: VGPRs, then LDS ----------------------------------------
   // Each thread moves NC chunks of a tile (chunk = 8 elements of one row: 16
@@ -222,9 +234,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       const int r = p * C::RPP + srow, u = sch + C::TPR * j;
       chunk_t v{};
       if ((kBI % C::RPP == 0 || r < kBI) && (C::CPR % C::TPR == 0 || u < C::CPR)) {
-        const int row = ti[r];
-        if (row >= 0)
-          v = *reinterpret_cast<const chunk_t*>(kvb + (size_t)row * DQK + C::TPR * j * 8);
+        // invalid slots hold -1 - (a valid row of the tile): load that row
+        // (finite data; the slot's score is masked and its p is exactly 0)
+        int row = ti[r];
+        row = row >= 0 ? row : -1 - row;
+        v = *reinterpret_cast<const chunk_t*>(kvb + (size_t)row * DQK + C::TPR * j * 8);
       }
       pre[k] = v;
     }
