@@ -137,6 +137,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   __shared__ int sIdx[kMaxK];           // sanitised indices (-1 = invalid), padded
   __shared__ int sList[kMaxK / kBI];    // tiles with a valid index, ascending
   __shared__ int sFirst[kMaxK / kBI];   // first valid index of each tile, or -1
+  __shared__ int sFull[kMaxK / kBI];    // all 32 indices of the tile are valid
   __shared__ float sSc[2][kBI];         // FP8: per-row scales of a tile
   __shared__ int sNvt;
   __shared__ int sFlag[2];  // a score above its reference + slack, by tile parity
@@ -166,11 +167,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       const int t = t0 + lane;
       int first = -1;
       if (t < ntiles) {
+        bool full = true;
         for (int r = kBI - 1; r >= 0; --r) {
           const int v = sIdx[t * kBI + r];
           first = v >= 0 ? v : first;
+          full = full && v >= 0;
         }
         sFirst[t] = first;
+        sFull[t] = full;
       }
       const bool f = first >= 0;
       const uint64_t m = __ballot(f);
@@ -318,28 +322,48 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         if (kSchedBarrier) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    const int* ti = sIdx + tile * kBI + 4 * g;
-    float sv[HT][8];
+    // tv = score * sm_scale * log2(e) - reference (log2 units), -inf when masked
+    float tv[HT][8];
     bool over = false;
+    if ((mode == 2 || (mode == 0 && it > 0)) && sFull[tile]) {
+      // steady state on a tile whose 32 indices are all valid: no masking
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      float mx = -INFINITY;
+      for (int ht = 0; ht < HT; ++ht) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int jj = (i < 4 ? 0 : 16) + (i & 3);
-        const float scl = FP8 ? sS[jj + 4 * g] * scale_log2 : scale_log2;
-        const float raw = s[i >> 2][ht][i & 3];
-        const float x = ti[jj] >= 0 ? raw * scl : -INFINITY;
-        sv[ht][i] = x;
-        mx = fmaxf(mx, x);
+        for (int i = 0; i < 8; ++i) {
+          const int jj = (i < 4 ? 0 : 16) + (i & 3);
+          const float scl = FP8 ? sS[jj + 4 * g] * scale_log2 : scale_log2;
+          tv[ht][i] = fmaf(s[i >> 2][ht][i & 3], scl, -m[ht]);
+          mx = fmaxf(mx, tv[ht][i]);
+        }
+        over = over || (mode == 0 && mx > kRefSlack);
       }
-      if (mode == 1 || (mode == 0 && it == 0)) {
-        mx = fmaxf(mx, wave_xor(mx, 16));
-        mx = fmaxf(mx, wave_xor(mx, 32));
-        // the first tile holds a valid index, so every head's max is finite
-        m[ht] = mode == 1 ? fmaxf(m[ht], mx) : mx;
-      } else if (mode == 0) {
-        over = over || (mx > m[ht] + kRefSlack);
+    } else {
+      const int* ti = sIdx + tile * kBI + 4 * g;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int jj = (i < 4 ? 0 : 16) + (i & 3);
+          const float scl = FP8 ? sS[jj + 4 * g] * scale_log2 : scale_log2;
+          const float raw = s[i >> 2][ht][i & 3];
+          const float x = ti[jj] >= 0 ? raw * scl : -INFINITY;
+          sv[i] = x;
+          mx = fmaxf(mx, x);
+        }
+        if (mode == 1 || (mode == 0 && it == 0)) {
+          mx = fmaxf(mx, wave_xor(mx, 16));
+          mx = fmaxf(mx, wave_xor(mx, 32));
+          // the first tile holds a valid index, so every head's max is finite
+          m[ht] = mode == 1 ? fmaxf(m[ht], mx) : mx;
+        } else if (mode == 0) {
+          over = over || (mx > m[ht] + kRefSlack);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tv[ht][i] = sv[i] - m[ht];
       }
     }
     if (mode == 1) return;
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       uint32_t pk[4];
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        float p0 = fast_exp2(sv[ht][i] - m[ht]), p1 = fast_exp2(sv[ht][i + 1] - m[ht]);
+        float p0 = fast_exp2(tv[ht][i]), p1 = fast_exp2(tv[ht][i + 1]);
         psum += p0 + p1;
         if constexpr (FP8) {
           p0 *= sS[(i < 4 ? 0 : 16) + 4 * g + (i & 3)];
