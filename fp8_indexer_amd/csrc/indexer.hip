@@ -41,16 +41,23 @@ constexpr int kKT = 64;                         // keys per LDS tile
 constexpr int kXcds = 8;
 constexpr int kMinChunk = 512;  // keys per chunk, at least
 
-template <int H, int D>
+// KP (key-parallel, for decode-like inputs with at most TW tokens per batch
+// entry): all waves of a workgroup hold the same tokens and each takes one
+// 16-key sub-tile of every key tile, instead of each wave owning its tokens.
+template <int H, int D, bool KP>
 struct IdxCfg {
   static_assert(H == 4 || H == 8 || H == 16 || H == 32 || H == 64 || H == 128, "H");
   static_assert(D == 64 || D == 128 || D == 256, "D");
   static constexpr int TW = kRowsPerWave / H;  // tokens per wave
-  static constexpr int TB = TW * kIdxWaves;    // tokens per workgroup
+  static constexpr int TB = KP ? TW : TW * kIdxWaves;  // tokens per workgroup
   static constexpr int KS = (D + 127) / 128;   // 128-deep MFMA steps
   static constexpr int CPR = D / 16;           // 16-byte chunks per key row
-  static constexpr int TILE_BYTES = kKT * D;
-  static constexpr int CHUNKS = kKT * CPR;
+  // keys per LDS tile: larger when streaming a long key range per token
+  // (more bytes in flight per workgroup), NS 16-key sub-tiles per wave
+  static constexpr int KT = KP ? 256 : kKT;
+  static constexpr int NS = KP ? KT / 16 / kIdxWaves : KT / 16;
+  static constexpr int TILE_BYTES = KT * D;
+  static constexpr int CHUNKS = KT * CPR;
   static constexpr int CPT = (CHUNKS + kIdxThreads - 1) / kIdxThreads;
   // Row placement: C element (row tile rt, lane group g, i) holds the row
   // with group-major index L = 32*g + 4*rt + i, i.e. token L / H, head L % H.
@@ -123,35 +130,42 @@ __device__ __forceinline__ int tile_off(int kk, int c) {
   return kk * D + ((c ^ (kk % CPR)) << 4);
 }
 
-template <int H, int D>
+template <int H, int D, bool KP>
 __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int* __restrict__ ks,
     const int* __restrict__ ke, float* __restrict__ logits, int M, int N,
     int n_tblocks, int n_tblocks_pad, int n_chunks, int chunk_keys) {
-  using C = IdxCfg<H, D>;
+  using C = IdxCfg<H, D, KP>;
+  static_assert(!KP || (C::KT / 16) % kIdxWaves == 0, "key-parallel: whole sub-tiles per wave");
+  static_assert(C::KT <= kIdxThreads, "one key scale per thread");
   __shared__ __align__(16) uint8_t sK[2][C::TILE_BYTES];
-  __shared__ float sKs[2][kKT];
+  __shared__ float sKs[2][C::KT];
   __shared__ int sRed[2][kIdxWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // ---- item id -> (batch, token block, key chunk), XCD-aware -------------
+  // ---- item id -> (batch, token block, key chunk) ------------------------
+  // With at least kXcds token blocks, all chunks of a block go to one XCD
+  // (ids = xcd mod kXcds; consecutive workgroups are dealt round-robin to
+  // the XCDs), keeping its q in one L2; with fewer (decode), ids map
+  // directly so that the chunks spread over every XCD.
   const int per_batch = n_tblocks_pad * n_chunks;
   const int b = blockIdx.x / per_batch;
   const int id = blockIdx.x % per_batch;
+  const bool xcd_map = n_tblocks_pad % kXcds == 0 && n_tblocks >= kXcds;
   const int xcd = id % kXcds;
-  const int chunk = (id / kXcds) % n_chunks;
-  const int tb_rev = (id / (kXcds * n_chunks)) * kXcds + xcd;
+  const int chunk = xcd_map ? (id / kXcds) % n_chunks : id % n_chunks;
+  const int tb_rev = xcd_map ? (id / (kXcds * n_chunks)) * kXcds + xcd : id / n_chunks;
   const int tb = n_tblocks_pad - 1 - tb_rev;  // latest tokens first
   if (tb < 0 || tb >= n_tblocks) return;
   const int t0 = tb * C::TB;
 
   // ---- this wave's tokens: q fragments and effective weights (issued
   // before the window reduction, which they do not depend on) ------------
-  const int tw0 = t0 + wave * C::TW;
+  const int tw0 = KP ? t0 : t0 + wave * C::TW;
   i32x8 qf[kRT][C::KS];
   float weff[kRT][4];
 #pragma unroll
@@ -248,11 +262,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   const bool store_lane = (g % C::GPT) == 0;
 
   // ---- K tile staging -----------------------------------------------------
-  const int ntiles = (c1 - c0 + kKT - 1) / kKT;
+  const int ntiles = (c1 - c0 + C::KT - 1) / C::KT;
   i32x4 pre[C::CPT];
   float pks = 0.f;
   auto gload = [&](int tile) {
-    const int kb = c0 + tile * kKT;
+    const int kb = c0 + tile * C::KT;
 #pragma unroll
     for (int j = 0; j < C::CPT; ++j) {
       const int ch = tid + j * kIdxThreads;
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       }
       pre[j] = v;
     }
-    if (tid < kKT) {
+    if (tid < C::KT) {
       const int key = kb + tid;
       pks = key < c1 ? k_scale[(size_t)b * N + key] : 0.f;
     }
@@ -276,7 +290,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       if (ch < C::CHUNKS)
         *reinterpret_cast<i32x4*>(&sK[buf][tile_off<D>(ch / C::CPR, ch % C::CPR)]) = pre[j];
     }
-    if (tid < kKT) sKs[buf][tid] = pks;
+    if (tid < C::KT) sKs[buf][tid] = pks;
   };
 
   gload(0);
@@ -285,10 +299,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
 
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
-    const int kb = c0 + tile * kKT;
+    const int kb = c0 + tile * C::KT;
     if (tile + 1 < ntiles) gload(tile + 1);
     // skip waves whose tokens do not see this tile
-    if (wmax > kb && wmin < kb + kKT) {
+    if (wmax > kb && wmin < kb + C::KT) {
       // 16-key sub-tiles, software pipelined (128-deep keys): the MFMAs of
       // sub-tile n+1 are issued before the epilogue of sub-tile n
       constexpr int NB = C::KS == 1 ? 2 : 1;
@@ -336,18 +350,21 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
         for (int j = 0; j < C::TPL; ++j)
           if (store_lane && key >= ls[j] && key < le[j]) orow[j][key] = sum[j] * ksc;
       };
+      // this wave's sub-tiles: all of them, or (key-parallel) every
+      // kIdxWaves-th one
+      auto sub = [&](int j) { return KP ? j * kIdxWaves + wave : j; };
       if constexpr (NB == 2) {
-        mm(0, acc[0]);
+        mm(sub(0), acc[0]);
 #pragma unroll
-        for (int n = 0; n < kKT / 16; ++n) {
-          if (n + 1 < kKT / 16) mm(n + 1, acc[(n + 1) & 1]);
-          epi(n, acc[n & 1]);
+        for (int j = 0; j < C::NS; ++j) {
+          if (j + 1 < C::NS) mm(sub(j + 1), acc[(j + 1) & 1]);
+          epi(sub(j), acc[j & 1]);
         }
       } else {
 #pragma unroll 1
-        for (int n = 0; n < kKT / 16; ++n) {
-          mm(n, acc[0]);
-          epi(n, acc[0]);
+        for (int j = 0; j < C::NS; ++j) {
+          mm(sub(j), acc[0]);
+          epi(sub(j), acc[0]);
         }
       }
     }
@@ -356,11 +373,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   }
 }
 
-template <int H, int D>
-hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
-  using C = IdxCfg<H, D>;
+template <int H, int D, bool KP>
+hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
+  using C = IdxCfg<H, D, KP>;
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
-  const int n_tblocks_pad = (n_tblocks + kXcds - 1) / kXcds * kXcds;
+  const int n_tblocks_pad =
+      n_tblocks >= kXcds ? (n_tblocks + kXcds - 1) / kXcds * kXcds : n_tblocks;
   // Key chunks: a chunk reloads its token block's q, so blocks are split
   // only as far as needed to give every workgroup slot of the device an item
   // (decode-like inputs with few token blocks), with chunks of >= 512 keys.
@@ -377,15 +395,22 @@ hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
   const long long want = (slots + tblocks - 1) / tblocks;
   const int n_chunks0 = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
   int chunk_keys = (int)((a.N + n_chunks0 - 1) / n_chunks0);
-  chunk_keys = (chunk_keys + kKT - 1) / kKT * kKT;
+  chunk_keys = (chunk_keys + C::KT - 1) / C::KT * C::KT;
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
   const long long blocks = (long long)a.B * n_tblocks_pad * n_chunks;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((indexer_logits_kernel<H, D>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
+  hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
                      stream, (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                      a.ks, a.ke, a.logits, (int)a.M, (int)a.N, n_tblocks, n_tblocks_pad, n_chunks,
                      chunk_keys);
   return hipGetLastError();
+}
+
+// Few tokens per batch entry (decode): the key-parallel layout.
+template <int H, int D>
+hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
+  if (a.M * H <= kRowsPerWave) return launch_kp<H, D, true>(a, stream);
+  return launch_kp<H, D, false>(a, stream);
 }
 
 }  // namespace
