@@ -130,7 +130,8 @@ template <int DQK, int DV, bool FP8, int NW, int HPW>
 __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_, const float* __restrict__ kv_scale,
     const float* __restrict__ sink, const int* __restrict__ idx, uint16_t* __restrict__ o, int M,
-    int N, int Hq, int K, float scale_log2) {
+    int N, int Hq, int K, float scale_log2, int S, int kspan, float* __restrict__ wso,
+    float2* __restrict__ wsml) {
   using C = AttnCfg<DQK, DV, FP8, NW, HPW>;
   constexpr int HT = C::HT, PG = C::PG, OH = C::OH, OTW = C::OTW;
   __shared__ __align__(16) uint16_t sKV[2][C::TILE];
@@ -147,15 +148,20 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int rtok = (int)(gridDim.x - 1 - blockIdx.x);  // (b, t) row, latest first
+  // workgroup -> (b, t) row, latest first, and split s of its K indices:
+  // [s*kspan, s*kspan + klen) (S = 1: the whole row)
+  const int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
+  const int split = (int)(blockIdx.x % S);
   const int b = rtok / M;
-  const int ntiles = (K + kBI - 1) / kBI;
+  const int kbeg = split * kspan;
+  const int klen = max(0, min(K - kbeg, kspan));
+  const int ntiles = (klen + kBI - 1) / kBI;
 
   // ---- indices -> LDS, list of tiles holding a valid index -----------------
   {
-    const int* ridx = idx + (size_t)rtok * K;
+    const int* ridx = idx + (size_t)rtok * K + kbeg;
     for (int p = tid; p < ntiles * kBI; p += C::THREADS) {
-      const int v = p < K ? ridx[p] : -1;
+      const int v = p < klen ? ridx[p] : -1;
       sIdx[p] = (v >= 0 && v < N) ? v : -1;
     }
   }
@@ -501,6 +507,19 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       mf[k] = sM[(wave / PG) * PG + k][col];
     }
   }
+  if (wso) {
+    // split: unnormalised O, and (m, l) of each head, for the merge kernel
+    const size_t part = (size_t)rtok * S + split;
+#pragma unroll
+    for (int oh = 0; oh < OH; ++oh) {
+      const int h = PG > 1 ? (wave / PG) * PG * 16 + oh * 16 + col : h0 + 16 * oh;
+      float* orow = wso + (part * Hq + h) * DV + c0 + g * 4;
+#pragma unroll
+      for (int t = 0; t < OTW; ++t) *reinterpret_cast<f32x4*>(orow + t * 16) = oacc[oh][t];
+      if (g == 0 && wave % PG == 0) wsml[part * Hq + h] = float2{mf[oh], lf[oh]};
+    }
+    return;
+  }
 #pragma unroll
   for (int oh = 0; oh < OH; ++oh) {
     const int h = PG > 1 ? (wave / PG) * PG * 16 + oh * 16 + col : h0 + 16 * oh;
@@ -519,17 +538,111 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   }
 }
 
+// Merge of the splits of one row (one thread per head and 4 output
+// columns): o = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s + e^sink 2^-M)
+// with M = max_s m_s -- the same value as one pass over all K indices,
+// since every split's O_s and l_s share its reference m_s.
+template <int DV>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ wso,
+                                                         const float2* __restrict__ wsml,
+                                                         const float* __restrict__ sink,
+                                                         uint16_t* __restrict__ o, int Hq, int S) {
+  constexpr int TPH = DV / 4;        // threads per head
+  constexpr int HPB = 256 / TPH;     // heads per workgroup
+  static_assert(256 % TPH == 0, "DV");
+  const int hblocks = Hq / HPB;
+  const int row = blockIdx.x / hblocks;
+  const int h = (blockIdx.x % hblocks) * HPB + threadIdx.x / TPH;
+  const int cq = (threadIdx.x % TPH) * 4;
+  const size_t p0 = (size_t)row * S;
+  float mmax = -INFINITY;
+  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, wsml[(p0 + s) * Hq + h].x);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float2 ml = wsml[(p0 + s) * Hq + h];
+    const float wgt = fast_exp2(ml.x - mmax);
+    l += wgt * ml.y;
+    acc += wgt * *reinterpret_cast<const f32x4*>(wso + ((p0 + s) * Hq + h) * DV + cq);
+  }
+  if (sink) l += fast_exp2(sink[h] * kLog2e - mmax);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const f32x4 v = acc * inv;
+  uint2 pk2;
+  pk2.x = pack_bf16x2(v[0], v[1]);
+  pk2.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(o + ((size_t)row * Hq + h) * DV + cq) = pk2;
+}
+
+int device_cus() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    return v;
+  return 256;
+}
+
 template <int DQK, int DV, bool FP8, int NW, int HPW>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   using C = AttnCfg<DQK, DV, FP8, NW, HPW>;
   const long long rows = a.B * a.M;
   if (rows > 0x7fffffffLL || a.K > kMaxK || a.Hq != NW * HPW) return hipErrorInvalidValue;
   const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)DQK);
-  hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW>), dim3((unsigned)rows),
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // Few rows (decode): split each row's K indices over S workgroups (at
+  // least 4 tiles each) so that the device is filled, and merge.  The
+  // partial results live in a stream-ordered workspace; without one the
+  // rows run unsplit.
+  const int cus = device_cus();
+  int S = 1, kspan = a.K;
+  if (rows * 2 <= cus) {
+    const int want = (int)((cus + rows - 1) / rows);
+    const int max_s = max(1, a.K / (4 * kBI));
+    S = min(want, max_s);
+    kspan = (a.K + S - 1) / S;
+    kspan = (kspan + kBI - 1) / kBI * kBI;
+    S = (a.K + kspan - 1) / kspan;
+  }
+  void* ws = nullptr;
+  if (S > 1) {
+    // keep freed workspace in the device's default pool between calls
+    static bool pool_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !pool_set[dev]) {
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+      }
+      (void)hipGetLastError();
+      pool_set[dev] = true;
+    }
+    const size_t bytes = (size_t)rows * S * a.Hq * (DV * sizeof(float) + sizeof(float2));
+    if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      ws = nullptr;
+      S = 1;
+      kspan = a.K;
+    }
+  }
+  float* wso = static_cast<float*>(ws);
+  float2* wsml = ws ? reinterpret_cast<float2*>(wso + (size_t)rows * S * a.Hq * DV) : nullptr;
+  hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW>), dim3((unsigned)(rows * S)),
                      dim3(C::THREADS), 0, stream, (const uint16_t*)a.q, a.kv, a.kv_scale,
                      a.attn_sink, a.topk_idxs, (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K,
-                     (float)((double)scale * 1.4426950408889634));
-  return hipGetLastError();
+                     scale_log2, S, kspan, wso, wsml);
+  hipError_t err = hipGetLastError();
+  if (ws) {
+    if (err == hipSuccess) {
+      constexpr int HPB = 256 / (DV / 4);
+      hipLaunchKernelGGL((attn_merge_kernel<DV>), dim3((unsigned)(rows * (a.Hq / HPB))), dim3(256),
+                         0, stream, wso, wsml, a.attn_sink, (uint16_t*)a.o, a.Hq, S);
+      err = hipGetLastError();
+    }
+    const hipError_t ferr = hipFreeAsync(ws, stream);
+    if (err == hipSuccess) err = ferr;
+  }
+  return err;
 }
 
 // Heads per wave at 128 heads (tuning knob: 32 -> 4 waves, 16 -> 8 waves).

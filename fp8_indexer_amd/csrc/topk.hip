@@ -118,12 +118,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     const int pshift = shift + (round == 0 ? 12 : 10);  // bits above this digit
     for (int i = tid; i < nbins; i += kTkThreads) hist[i] = 0;
     __syncthreads();
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
+    auto count = [&](int c, uint32_t u) {
       const int i = s + c * kTkThreads + tid;
-      const uint32_t u = get(c);
       const bool match = i < e && (round == 0 || (u >> pshift) == prefix);
       if (match) atomicAdd(&hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+    };
+    if (resident) {
+#pragma unroll 1
+      for (int c = 0; c < nch; ++c) count(c, get(c));
+    } else {
+      // 8 loads in flight before their keys are counted
+#pragma unroll 1
+      for (int c0 = 0; c0 < nch; c0 += 8) {
+        uint32_t u[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = c0 + j < nch ? get(c0 + j) : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (c0 + j < nch) count(c0 + j, u[j]);
+      }
     }
     __syncthreads();
     // suffix counts: thread t owns bins [t*bpt, (t+1)*bpt)
@@ -152,42 +165,62 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   const int n_eq = K - above_total;  // keys equal to tau that are selected (>= 1)
 
   // ---- emission in index order -------------------------------------------
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int eq_run = 0, sel_run = 0;
+  // Wave w owns the contiguous segment [w*segw, (w+1)*segw) of the row (re-read
+  // from L2): it counts its keys above tau and equal to tau, one barrier
+  // exchanges the counts, then it writes its segment with ballots.
+  const int segw = (len + kTkWaves * kWave - 1) / (kTkWaves * kWave) * kWave;
+  const int wb = wave * segw;
+  auto key_at = [&](int i) -> uint32_t { return i < len ? order_key(row[s + i]) : 0u; };
+  int gtc = 0, eqc = 0;
 #pragma unroll 1
-  for (int c = 0; c < nch; ++c) {
-    const int i = s + c * kTkThreads + tid;
-    const uint32_t u = get(c);
-    const bool valid = i < e;
-    const bool gt = valid && u > tau;
-    const bool eq = valid && u == tau;
-    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
-    if (lane == 0) {
-      sCnt[0][wave] = __popcll(mgt);
-      sCnt[1][wave] = __popcll(meq);
-    }
-    __syncthreads();
-    int gt_off = 0, eq_off = 0, gt_tot = 0, eq_tot = 0;
+  for (int c0 = 0; c0 < segw; c0 += 8 * kWave) {
+    uint32_t u[8];
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const int a = sCnt[0][w], b = sCnt[1][w];
-      gt_off += w < wave ? a : 0;
-      eq_off += w < wave ? b : 0;
-      gt_tot += a;
-      eq_tot += b;
+    for (int j = 0; j < 8; ++j) u[j] = key_at(wb + c0 + j * kWave + lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = wb + c0 + j * kWave + lane;
+      const bool in = c0 + j * kWave < segw && i < len;
+      gtc += (int)__popcll(__ballot(in && u[j] > tau));
+      eqc += (int)__popcll(__ballot(in && u[j] == tau));
     }
-    const int gt_before = gt_off + __popcll(mgt & lt_mask);
-    const int eq_before = eq_off + __popcll(meq & lt_mask);
+  }
+  if (lane == 0) {
+    sCnt[0][wave] = gtc;
+    sCnt[1][wave] = eqc;
+  }
+  __syncthreads();
+  int gt_base = 0, eq_base = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    gt_base += w < wave ? sCnt[0][w] : 0;
+    eq_base += w < wave ? sCnt[1][w] : 0;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_run = eq_base, sel_run = gt_base + min(eq_base, n_eq);
+#pragma unroll 1
+  for (int c0 = 0; c0 < segw; c0 += 8 * kWave) {
+   uint32_t uu[8];
+#pragma unroll
+   for (int j = 0; j < 8; ++j) uu[j] = key_at(wb + c0 + j * kWave + lane);
+#pragma unroll
+   for (int j = 0; j < 8; ++j) {
+    const int i = wb + c0 + j * kWave + lane;
+    const bool in = c0 + j * kWave < segw && i < len;
+    const uint32_t u = uu[j];
+    const bool gt = in && u > tau;
+    const bool eq = in && u == tau;
+    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+    const int eq_before = (int)__popcll(meq & lt_mask);
     const int eq_left = max(0, n_eq - eq_run);
     const bool eq_sel = eq && eq_before < eq_left;
-    const int pos = sel_run + gt_before + min(eq_before, eq_left);
-    if ((gt || eq_sel) && pos < K) o[pos] = i;  // pos < K always; guard is defensive
-    sel_run += gt_tot + min(eq_tot, eq_left);
-    eq_run += eq_tot;
-    __syncthreads();
+    const int pos = sel_run + (int)__popcll(mgt & lt_mask) + min(eq_before, eq_left);
+    if ((gt || eq_sel) && pos < K) o[pos] = s + i;
+    sel_run += (int)__popcll(mgt) + min((int)__popcll(meq), eq_left);
+    eq_run += (int)__popcll(meq);
+   }
   }
 }
-
 
 // ---- four waves per row ----------------------------------------------------
 // For rows of at most 256*KR keys: wave w holds the contiguous segment

@@ -18,7 +18,9 @@
  *    waits for its kernels and reports their errors.
  *  * Ownership: the caller allocates and owns every buffer, including the
  *    intermediates of dsa_prefill.  The library keeps no pointer after a call
- *    returns and allocates no device memory.  Calls are thread-safe.
+ *    returns.  The only device memory it takes is the stream-ordered
+ *    temporary of dsa_sparse_attn_fwd (and dsa_prefill) for few query rows,
+ *    described there.  Calls are thread-safe.
  *  * Errors: arguments are checked on the host before anything is enqueued.
  *    NULL pointers, non-positive sizes, misalignment or inconsistent sizes
  *    give DSA_ERR_INVALID_VALUE; a valid shape with no compiled kernel gives
@@ -131,8 +133,15 @@ dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
  *   topk_idxs  [B, M, K] int32
  *   o          [B, M, Hq, Dv] bf16 output
  *   sm_scale   softmax scale; <= 0 selects 1/sqrt(Dqk)
- * Supported: Hq a multiple of 16 up to 256; (Dqk, Dv) in {(64, 64), (576, 512)};
- * 1 <= K <= 4096; Dv <= Dqk.
+ * Supported: Hq in {16, 32, 64, 128}; (Dqk, Dv) in {(64, 64), (576, 512)}
+ * (FP8 kv with (576, 512) only); 1 <= K <= 4096.
+ * Few query rows (B*M at most half the device's compute units, as in
+ * decode): each row's K indices are split over several workgroups whose
+ * partial results are merged by a second kernel; the partials live in a
+ * temporary taken with hipMallocAsync on `stream` from the device's default
+ * memory pool (B*M*splits*Hq*(4*Dv + 8) bytes, splits <= K/128) and freed
+ * with hipFreeAsync on the same stream.  If that allocation fails, the rows
+ * run unsplit with the same result.
  */
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
                                dsa_kv_dtype kv_dtype, const float* kv_scale,
