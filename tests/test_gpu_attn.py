@@ -140,3 +140,24 @@ def test_attn_reference_restart(fp8, where):
     ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
                              kv_scale=x["kv_scale"])
     check_attn(o, ref, f"restart/{where}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_attn_split_rows_edge_cases(fp8):
+    """Few rows with K = 2048: each row's indices are split over several
+    workgroups and merged.  Row 0 has no valid index (zero output), row 1
+    only valid indices in the last split, row 2 a full set."""
+    B, M, N, K = 1, 3, 5000, 2048
+    wl = W.Workload("s", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, kv_fp8=fp8,
+                    seed=9)
+    log(f"attn split edge fp8={fp8}")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(5)
+    idx = np.full((B, M, K), -1, np.int32)
+    idx[0, 1, K - 100:] = rng.choice(N, size=100, replace=False)
+    idx[0, 2, :] = rng.choice(N, size=K, replace=False)
+    o = _run(x, idx, wl)
+    assert torch.all(o[0, 0].float() == 0)
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
+                             kv_scale=x["kv_scale"])
+    check_attn(o, ref, "split edge")
