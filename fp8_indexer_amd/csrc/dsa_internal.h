@@ -45,6 +45,21 @@ struct AttnArgs {
 bool indexer_supported(int H, int D);
 bool attn_supported(int Hq, int Dqk, int Dv, bool fp8);
 
+// Stream-ordered temporaries (hipMallocAsync) come from the current device's
+// default memory pool; keep freed blocks in the pool between calls.
+inline void keep_pool_memory() {
+  static bool done[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    uint64_t thr = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+  }
+  (void)hipGetLastError();
+  done[dev] = true;
+}
+
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);

@@ -605,18 +605,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   }
   void* ws = nullptr;
   if (S > 1) {
-    // keep freed workspace in the device's default pool between calls
-    static bool pool_set[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !pool_set[dev]) {
-      hipMemPool_t pool;
-      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-        uint64_t thr = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
-      }
-      (void)hipGetLastError();
-      pool_set[dev] = true;
-    }
+    keep_pool_memory();
     const size_t bytes = (size_t)rows * S * a.Hq * (DV * sizeof(float) + sizeof(float2));
     if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) {
       (void)hipGetLastError();

@@ -246,33 +246,23 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-template <int KR>
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
-                                                               const int* __restrict__ ks,
-                                                               const int* __restrict__ ke,
-                                                               int* __restrict__ out, int N, int K) {
+// Writes to o[0..K) the positions (first + i, or cand[i] when GATHER) of the
+// K largest of len > K keys src[i] (or src[cand[i]]), i < len, in ascending
+// order of i.  Keys at most 256*KR.  Workgroup of kRowThreads; the LDS
+// arrays are the caller's.
+template <int KR, bool GATHER>
+__device__ __forceinline__ void row_select(const float* __restrict__ src,
+                                           const int* __restrict__ cand, int len, int first,
+                                           int K, int* __restrict__ o, uint32_t* hist, int* sRed,
+                                           int* sSel, int (*sCnt)[kRowWaves]) {
   constexpr int SEG = kWave * KR;
-  __shared__ __align__(16) uint32_t hist[2048];
-  __shared__ int sRed[kRowWaves];
-  __shared__ int sSel[2];
-  __shared__ int sCnt[2][kRowWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t r = blockIdx.x;
-  const int s = clampi(ks[r], 0, N);
-  const int e = clampi(ke[r], s, N);
-  const int len = e - s;
-  int* o = out + r * (size_t)K;
-  if (len <= K) {
-    for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
-    return;
-  }
-  const float* row = logits + r * (size_t)N + s;
   const int base = wave * SEG;
   uint32_t keys[KR];
 #pragma unroll
   for (int c = 0; c < KR; ++c) {
     const int i = base + c * kWave + lane;
-    keys[c] = i < len ? order_key(row[i]) : 0u;
+    keys[c] = i < len ? order_key(GATHER ? src[cand[i]] : src[i]) : 0u;
   }
 
   uint32_t prefix = 0;
@@ -360,11 +350,100 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     const int eq_left = max(0, n_eq - eq_run);
     const bool eq_sel = eq && eq_before < eq_left;
     const int pos = sel_run + __popcll(mgt & lt_mask) + min(eq_before, eq_left);
-    if ((gt || eq_sel) && pos < K) o[pos] = s + i;
+    if ((gt || eq_sel) && pos < K) o[pos] = GATHER ? cand[i] : first + i;
     sel_run += __popcll(mgt) + min((int)__popcll(meq), eq_left);
     eq_run += __popcll(meq);
   }
 }
+
+#define DSA_TOPK_LDS                                  \
+  __shared__ __align__(16) uint32_t hist[2048];       \
+  __shared__ int sRed[kRowWaves];                     \
+  __shared__ int sSel[2];                             \
+  __shared__ int sCnt[2][kRowWaves];
+
+template <int KR>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
+                                                               const int* __restrict__ ks,
+                                                               const int* __restrict__ ke,
+                                                               int* __restrict__ out, int N, int K) {
+  DSA_TOPK_LDS
+  const int tid = threadIdx.x;
+  const size_t r = blockIdx.x;
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  const int len = e - s;
+  int* o = out + r * (size_t)K;
+  if (len <= K) {
+    for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
+    return;
+  }
+  row_select<KR, false>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel, sCnt);
+}
+
+// ---- long rows in two levels ----------------------------------------------
+// Level 1: the row is cut into segments of kSegKeys keys and each segment's
+// own top-K (or the whole segment if it is shorter) is written, in ascending
+// index order, to K candidate slots per segment.  A key among the K first of
+// the row in (value descending, index ascending) order has fewer than K keys
+// ranked above it in the whole row, hence in its segment: the candidates
+// hold the row's selection.  Level 2 selects the K first of the candidates
+// (ranked by their logits, read back by index), whose storage order is the
+// index order.
+constexpr int kSegKeys = kRowThreads * 32;
+
+__global__ __launch_bounds__(kRowThreads) void topk_seg_kernel(const float* __restrict__ logits,
+                                                               const int* __restrict__ ks,
+                                                               const int* __restrict__ ke,
+                                                               int* __restrict__ cand, int N, int K,
+                                                               int nseg) {
+  DSA_TOPK_LDS
+  const int tid = threadIdx.x;
+  const size_t r = blockIdx.x / nseg;
+  const int seg = (int)(blockIdx.x % nseg);
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  if (e - s <= K) return;  // level 2 writes short rows directly
+  const int s0 = s + seg * kSegKeys;
+  const int len = min(e - s0, kSegKeys);
+  if (len <= 0) return;
+  int* o = cand + (r * nseg + seg) * (size_t)K;
+  if (len <= K) {
+    for (int i = tid; i < len; i += kRowThreads) o[i] = s0 + i;
+    return;
+  }
+  row_select<32, false>(logits + r * (size_t)N + s0, nullptr, len, s0, K, o, hist, sRed, sSel, sCnt);
+}
+
+template <int KR>
+__global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __restrict__ logits,
+                                                                 const int* __restrict__ ks,
+                                                                 const int* __restrict__ ke,
+                                                                 const int* __restrict__ cand,
+                                                                 int* __restrict__ out, int N, int K,
+                                                                 int nseg) {
+  DSA_TOPK_LDS
+  const int tid = threadIdx.x;
+  const size_t r = blockIdx.x;
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  const int len = e - s;
+  int* o = out + r * (size_t)K;
+  if (len <= K) {
+    for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
+    return;
+  }
+  // candidates: K per full segment, min(K, rest) for the last, contiguous
+  const int ns = (len + kSegKeys - 1) / kSegKeys;
+  const int n = (ns - 1) * K + min(K, len - (ns - 1) * kSegKeys);
+  const int* c = cand + r * nseg * (size_t)K;
+  if (n <= K) {  // a single segment of more than K keys: already selected
+    for (int i = tid; i < K; i += kRowThreads) o[i] = c[i];
+    return;
+  }
+  row_select<KR, true>(logits + r * (size_t)N, c, n, 0, K, o, hist, sRed, sSel, sCnt);
+}
+
 
 }  // namespace
 
@@ -381,6 +460,38 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
                        a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
     return hipGetLastError();
+  }
+  // longer rows: two levels through a stream-ordered candidate buffer while
+  // the candidates of a row fit one workgroup's registers
+  const int nseg = (int)((a.N + kSegKeys - 1) / kSegKeys);
+  const long long ncand = (long long)nseg * a.K;
+  if (a.K <= kSegKeys && ncand <= kRowThreads * 64 && rows * nseg <= 0x7fffffffLL) {
+    keep_pool_memory();
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)rows * ncand * sizeof(int), stream) == hipSuccess) {
+      int* cand = static_cast<int*>(ws);
+      hipLaunchKernelGGL(topk_seg_kernel, dim3((unsigned)(rows * nseg)), dim3(kRowThreads), 0,
+                         stream, a.logits, a.ks, a.ke, cand, (int)a.N, (int)a.K, nseg);
+      hipError_t err = hipGetLastError();
+      if (err == hipSuccess) {
+        if (ncand <= kRowThreads * 16)
+          hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                             nseg);
+        else if (ncand <= kRowThreads * 32)
+          hipLaunchKernelGGL(topk_merge_kernel<32>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                             nseg);
+        else
+          hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                             nseg);
+        err = hipGetLastError();
+      }
+      const hipError_t ferr = hipFreeAsync(ws, stream);
+      return err != hipSuccess ? err : ferr;
+    }
+    (void)hipGetLastError();
   }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a.logits,
                      a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);

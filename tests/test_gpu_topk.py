@@ -108,3 +108,17 @@ def test_topk_workloads(name, nrows):
     _compare(lg, ks, ke, wl.K, rows=rows, what=name)
     lg_t = W.synthetic_logits(wl, ties=True).numpy()
     _compare(lg_t, ks, ke, wl.K, rows=rows, what=name + "/ties")
+
+
+@pytest.mark.parametrize("kind", ["special", "ties", "narrow"])
+@pytest.mark.parametrize("K", [100, 2048, 4096])
+def test_topk_two_level_rows(kind, K):
+    """N in (8192, 65536]: long rows are cut into 8192-key segments whose
+    top-K candidates are then reduced; lengths straddle segment boundaries."""
+    rng = np.random.default_rng(K + len(kind))
+    B, M, N = 1, 8, 40000
+    lg = _dist(kind, (B, M, N), rng)
+    ks = np.array([[0, 0, 0, 0, 0, 100, 31000, 5]], np.int32)
+    ke = np.array([[N, K + 1, 8192, 8193, 16384 + 7, 24000, N, 5 + K]], np.int32)
+    log(f"topk two-level {kind} K={K}")
+    _compare(lg, ks, ke, K, what=f"two-level {kind}/K{K}")
