@@ -135,8 +135,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int* __restrict__ ks,
-    const int* __restrict__ ke, float* __restrict__ logits, int M, int N,
-    int n_tblocks, int n_tblocks_pad, int n_chunks, int chunk_keys) {
+    const int* __restrict__ ke, float* __restrict__ logits, int M, int N, int B,
+    int n_tblocks, int n_chunks, int chunk_keys) {
   using C = IdxCfg<H, D, KP>;
   static_assert(!KP || (C::KT / 16) % kIdxWaves == 0, "key-parallel: whole sub-tiles per wave");
   static_assert(C::KT <= kIdxThreads, "one key scale per thread");
@@ -147,20 +147,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // ---- item id -> (batch, token block, key chunk) ------------------------
-  // With at least kXcds token blocks, all chunks of a block go to one XCD
-  // (ids = xcd mod kXcds; consecutive workgroups are dealt round-robin to
-  // the XCDs), keeping its q in one L2; with fewer (decode), ids map
-  // directly so that the chunks spread over every XCD.
-  const int per_batch = n_tblocks_pad * n_chunks;
-  const int b = blockIdx.x / per_batch;
-  const int id = blockIdx.x % per_batch;
-  const bool xcd_map = n_tblocks_pad % kXcds == 0 && n_tblocks >= kXcds;
-  const int xcd = id % kXcds;
-  const int chunk = xcd_map ? (id / kXcds) % n_chunks : id % n_chunks;
-  const int tb_rev = xcd_map ? (id / (kXcds * n_chunks)) * kXcds + xcd : id / n_chunks;
-  const int tb = n_tblocks_pad - 1 - tb_rev;  // latest tokens first
-  if (tb < 0 || tb >= n_tblocks) return;
+  // ---- one item: (batch b, token block tb, key chunk) ---------------------
+  auto process = [&](const int b, const int tb, const int chunk) {
   const int t0 = tb * C::TB;
 
   // ---- this wave's tokens: q fragments and effective weights (issued
@@ -371,17 +359,40 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     if (tile + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }
+  };
+
+  if constexpr (KP) {
+    // decode: one item per workgroup, items in id order (chunks of a batch
+    // entry spread over the XCDs)
+    const int per_batch = n_tblocks * n_chunks;
+    const int id = blockIdx.x % per_batch;
+    process(blockIdx.x / per_batch, n_tblocks - 1 - id / n_chunks, id % n_chunks);
+  } else {
+    // Persistent: items are numbered chunk-major, latest token blocks first
+    // (descending work for causal-like windows), and workgroup g takes items
+    // g, 2G-1-g, 2G+g, ... (a snake over rounds), which pairs long items with
+    // short ones.
+    const int G = (int)gridDim.x, per_chunk = B * n_tblocks;
+    const int n_items = per_chunk * n_chunks;
+    for (int rnd = 0;; ++rnd) {
+      const int item = rnd * G + ((rnd & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+      if (item >= n_items) break;
+      __syncthreads();  // the previous item's LDS reads are complete
+      const int rem = item % per_chunk;
+      process(rem % B, n_tblocks - 1 - rem / B, item / per_chunk);
+    }
+  }
 }
 
 template <int H, int D, bool KP>
 hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   using C = IdxCfg<H, D, KP>;
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
-  const int n_tblocks_pad =
-      n_tblocks >= kXcds ? (n_tblocks + kXcds - 1) / kXcds * kXcds : n_tblocks;
   // Key chunks: a chunk reloads its token block's q, so blocks are split
   // only as far as needed to give every workgroup slot of the device an item
   // (decode-like inputs with few token blocks), with chunks of >= 512 keys.
+  // The persistent layout wants two items per workgroup, so that the snake
+  // schedule can pair long windows with short ones.
   int cus = 256;
   {
     int dev = 0, v = 0;
@@ -392,16 +403,17 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   const long long slots = (long long)cus * (8 / kIdxWaves);  // 2 waves per SIMD, 4 SIMDs
   const long long tblocks = (long long)a.B * n_tblocks;
   const long long max_chunks = (a.N + kMinChunk - 1) / kMinChunk;
-  const long long want = (slots + tblocks - 1) / tblocks;
+  const long long want = ((KP ? 1 : 2) * slots + tblocks - 1) / tblocks;
   const int n_chunks0 = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
   int chunk_keys = (int)((a.N + n_chunks0 - 1) / n_chunks0);
   chunk_keys = (chunk_keys + C::KT - 1) / C::KT * C::KT;
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
-  const long long blocks = (long long)a.B * n_tblocks_pad * n_chunks;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long items = tblocks * n_chunks;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long blocks = KP ? items : (items < slots ? items : slots);
   hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
                      stream, (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
-                     a.ks, a.ke, a.logits, (int)a.M, (int)a.N, n_tblocks, n_tblocks_pad, n_chunks,
+                     a.ks, a.ke, a.logits, (int)a.M, (int)a.N, (int)a.B, n_tblocks, n_chunks,
                      chunk_keys);
   return hipGetLastError();
 }
