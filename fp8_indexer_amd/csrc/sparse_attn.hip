@@ -53,7 +53,7 @@ constexpr int kBI = 32;      // gathered rows per tile
 constexpr int kKVPad = 16;   // row padding (elements): see the LDS layout note
 constexpr int kMaxK = 4096;  // largest supported top-k
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRefSlack = 16.f;  // scores may exceed the reference by 2^16
+constexpr float kPLimit = 0x1p40f;  // largest per-lane l (hence p) without a restart
 
 // LDS operand lookahead (k-steps) and scheduling barriers in the MFMA loops
 // (tuning knobs).
@@ -73,6 +73,9 @@ constexpr int kPG = DSA_ATTN_PG;
 // q k-steps read from LDS instead of registers (tuning knob; the last ones).
 #ifndef DSA_ATTN_QL
 #define DSA_ATTN_QL 6
+#endif
+#ifndef DSA_ATTN_QL32
+#define DSA_ATTN_QL32 5
 #endif
 constexpr bool kSchedBarrier = DSA_ATTN_SB != 0;
 
@@ -97,16 +100,48 @@ struct AttnCfg {
   static constexpr int QC = DQK / 32;              // 32-deep k-steps of QK
   // The last QL k-steps of q come from LDS (registers for 8 waves x 16 heads
   // hold O and the rest of q); only with 16 heads per wave.
-  static constexpr int QL = (HPW == 16 && NW == 8 && DSA_ATTN_QL < QC) ? DSA_ATTN_QL : 0;
+  static constexpr int QL = (HPW == 16 && NW == 8 && DSA_ATTN_QL < QC)   ? DSA_ATTN_QL
+                            : (HPW == 32 && NW == 4 && DSA_ATTN_QL32 < QC) ? DSA_ATTN_QL32
+                                                                            : 0;
   static constexpr int QR = QC - QL;               // k-steps of q kept in registers
   static constexpr int OT = DV / 16;               // 16-wide output tiles
   // P groups: PG waves (16 heads each) share their P fragments through LDS and
   // split the Dv columns, so each wave multiplies V for PG*16 heads over
   // DV/PG columns: OH head tiles x OTW column tiles of O per wave.
-  static constexpr int PG = (HPW == 16 && NW % kPG == 0 && OT % kPG == 0) ? kPG : 1;
+  static constexpr int PG = (NW % kPG == 0 && OT % kPG == 0) ? kPG : 1;
   static constexpr int OH = PG * HT;
   static constexpr int OTW = OT / PG;
 };
+
+// QK^T MFMAs with the accumulator pinned to VGPRs.  The O accumulators of PV
+// (compiler-scheduled MFMAs) then fill the AGPRs, which is what lets 32 heads
+// per wave fit: with every MFMA result in AGPRs, O and S together need more
+// than the 256 AGPRs of a wave.  Hazards the compiler cannot see through the
+// asm: the accumulator is tied (vdst = srcC, no register to reuse while the
+// MFMA still reads it), each MFMA is preceded by 2 wait states (VALU write ->
+// MFMA read), and qk_drain() gives the MFMA results 24 wait states before
+// any VALU reads them.
+#ifndef DSA_ATTN_QKASM
+#define DSA_ATTN_QKASM 1
+#endif
+__device__ __forceinline__ void qk_mfma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  if (DSA_ATTN_QKASM) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  } else {
+    acc = mfma_bf16_16x16x32(a, b, acc);
+  }
+}
+__device__ __forceinline__ void qk_drain(f32x4& x0, f32x4& x1) {
+  if (DSA_ATTN_QKASM) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
+}
+
+// Lane index computed afresh (an asm the compiler cannot merge with an
+// earlier copy of the same value).
+__device__ __forceinline__ int fresh_lane_id() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -126,7 +161,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 // (measured on gfx950: ~190 B/clk per CU; XOR-swizzling the units by row
 // halves it, and slows the transposing read by a quarter).
 
-template <int DQK, int DV, bool FP8, int NW, int HPW>
+template <int DQK, int DV, bool FP8, int NW, int HPW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_, const float* __restrict__ kv_scale,
     const float* __restrict__ sink, const int* __restrict__ idx, uint16_t* __restrict__ o, int M,
@@ -141,12 +176,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   __shared__ int sFull[kMaxK / kBI];    // all 32 indices of the tile are valid
   __shared__ float sSc[2][kBI];         // FP8: per-row scales of a tile
   __shared__ int sNvt;
-  __shared__ int sFlag[2];  // a score above its reference + slack, by tile parity
+  __shared__ int sFlag[1];  // a head's sum passed kPLimit: restart
   __shared__ __align__(16) bf16x8 sP[NW][HT][kWave];  // P B-fragments
-  __shared__ float sL[PG > 1 ? NW : 1][16], sM[PG > 1 ? NW : 1][16];
-  __shared__ __align__(16) bf16x8 sQ[C::QL > 0 ? C::QL : 1][NW][kWave];  // q B-fragments
+  __shared__ float sL[PG > 1 ? NW : 1][HT][16], sM[PG > 1 ? NW : 1][HT][16];
+  __shared__ float sSink[NW * HPW];     // attn_sink of each head
+  __shared__ __align__(16) bf16x8 sQ[C::QL > 0 ? C::QL : 1][NW][HT][kWave];  // q B-fragments
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: an SGPR
   const int g = lane >> 4, col = lane & 15;
   // workgroup -> (b, t) row, latest first, and split s of its K indices:
   // [s*kspan, s*kspan + klen) (S = 1: the whole row)
@@ -157,15 +194,57 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   const int klen = max(0, min(K - kbeg, kspan));
   const int ntiles = (klen + kBI - 1) / kBI;
 
-  // ---- indices -> LDS, list of tiles holding a valid index -----------------
-  {
-    const int* ridx = idx + (size_t)rtok * K + kbeg;
-    for (int p = tid; p < ntiles * kBI; p += C::THREADS) {
-      const int v = p < klen ? ridx[p] : -1;
-      sIdx[p] = (v >= 0 && v < N) ? v : -1;
-    }
+  // ---- prologue: every global load is issued before anything waits on one --
+  // indices (the first IB per thread; more for K > IB * THREADS)
+  const int* ridx = idx + (size_t)rtok * K + kbeg;
+  const int nidx = ntiles * kBI;
+  constexpr int IB = 8;
+  int iv[IB];
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int p = tid + j * C::THREADS;
+    iv[j] = p < klen ? ridx[p] : -1;
   }
+  // q fragments of this wave's heads; the last QL k-steps go to LDS below
+  const int h0 = wave * HPW + col;  // head of head-tile ht: h0 + 16*ht
+  bf16x8 qf[HT][C::QR];
+  bf16x8 ql[C::QL > 0 ? C::QL : 1][HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint16_t* qrow = q + ((size_t)rtok * Hq + h0 + 16 * ht) * DQK;
+#pragma unroll
+    for (int c = 0; c < C::QR; ++c)
+      qf[ht][c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + g * 8);
+#pragma unroll
+    for (int c = C::QR; c < C::QC; ++c)
+      ql[c - C::QR][ht] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + g * 8);
+  }
+  const float skv = (sink && tid < Hq) ? sink[tid] : 0.f;
+  const int c0 = (wave % PG) * (DV / PG);  // first output column of this wave
+  f32x4 oacc[OH][OTW];
+#pragma unroll
+  for (int oh = 0; oh < OH; ++oh)
+#pragma unroll
+    for (int t = 0; t < OTW; ++t) oacc[oh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[HT], lsum[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m[ht] = -1e30f;
+    lsum[ht] = 0.f;
+  }
+  // indices -> LDS (sanitised: -1 = invalid), sink -> LDS
+  auto sanitise = [&](int v) { return (v >= 0 && v < N) ? v : -1; };
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int p = tid + j * C::THREADS;
+    if (p < nidx) sIdx[p] = sanitise(iv[j]);
+  }
+  for (int p = tid + IB * C::THREADS; p < nidx; p += C::THREADS)
+    sIdx[p] = sanitise(p < klen ? ridx[p] : -1);
+  if (tid < Hq) sSink[tid] = skv;
   __syncthreads();
+  // list of tiles holding a valid index; first valid index of each tile
+  // (invalid slots gather that row: finite data whose p is exactly 0)
   if (wave == 0) {
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int base = 0;
@@ -183,74 +262,49 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         sFull[t] = full;
       }
       const bool f = first >= 0;
-      const uint64_t m = __ballot(f);
-      if (f) sList[base + __popcll(m & lt)] = t;
-      base += __popcll(m);
+      const uint64_t mk = __ballot(f);
+      if (f) sList[base + __popcll(mk & lt)] = t;
+      base += __popcll(mk);
     }
     if (lane == 0) sNvt = base;
   }
-
-  // ---- q fragments for this wave's heads -----------------------------------
-  const int h0 = wave * HPW + col;  // head of head-tile ht: h0 + 16*ht
-  bf16x8 qf[HT][C::QR];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const uint16_t* qrow = q + ((size_t)rtok * Hq + h0 + 16 * ht) * DQK;
+  for (int c = C::QR; c < C::QC; ++c)
 #pragma unroll
-    for (int c = 0; c < C::QR; ++c)
-      qf[ht][c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + g * 8);
-#pragma unroll
-    for (int c = C::QR; c < C::QC; ++c)
-      sQ[c - C::QR][wave][lane] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + g * 8);
-  }
-  const int c0 = (wave % PG) * (DV / PG);  // first output column of this wave
-  f32x4 oacc[OH][OTW];
-#pragma unroll
-  for (int oh = 0; oh < OH; ++oh)
-#pragma unroll
-    for (int t = 0; t < OTW; ++t) oacc[oh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[HT], lsum[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    m[ht] = -1e30f;
-    lsum[ht] = 0.f;
-  }
+    for (int ht = 0; ht < HT; ++ht) sQ[c - C::QR][wave][ht][lane] = ql[c - C::QR][ht];
   __syncthreads();
   const int nvt = sNvt;
-  // invalid slots of tiles with a valid index -> -1 - (first valid index)
-  for (int p = tid; p < ntiles * kBI; p += C::THREADS) {
-    const int first = sFirst[p / kBI];
-    if (sIdx[p] < 0 && first >= 0) sIdx[p] = -1 - first;
-  }
-  __syncthreads();
 
   // ---- tile staging: VGPRs, then LDS ----------------------------------------
   // Each thread moves NC chunks of a tile (chunk = 8 elements of one row: 16
-  // bytes of bf16 or 8 fp8 codes; invalid slots stage zeros).  The loads of
-  // the next tile are in flight while this wave multiplies P by V, the phase
-  // with registers to spare.
+  // bytes of bf16 or 8 fp8 codes).  The loads of tile it+1 are issued one by
+  // one between the QK^T k-steps of tile it and written to the other LDS
+  // buffer one by one between the PV column steps: a burst of gathers would
+  // hold up the issuing wave (the vector memory unit takes about 16 cycles
+  // per 64-lane 16-byte load) and, at one wave per SIMD, the SIMD with it.
   typedef typename std::conditional<FP8, uint2, i32x4>::type chunk_t;
   typedef typename std::conditional<FP8, uint8_t, uint16_t>::type elem_t;
   constexpr int NC = C::NC;
   chunk_t pre[NC];
+  int grow[C::PASSES];
   float pscale = 0.f;
   const int srow = tid / C::TPR, sch = tid % C::TPR;
   const elem_t* kvb = static_cast<const elem_t*>(kv_) + (size_t)b * N * DQK + sch * 8;
-  auto gload = [&](int tile) {
+  // chunk k: pass k / CPT (row slot p*RPP + srow), 16-byte unit sch + TPR*(k % CPT)
+  auto chunk_ok = [&](int k) {
+    const int r = (k / C::CPT) * C::RPP + srow, u = sch + C::TPR * (k % C::CPT);
+    return (kBI % C::RPP == 0 || r < kBI) && (C::CPR % C::TPR == 0 || u < C::CPR);
+  };
+  // rows of a tile's staging passes; invalid slots load the tile's first
+  // valid row (finite data; the slot's score is masked and its p is exactly 0)
+  auto gather_rows = [&](int tile) {
     const int* ti = sIdx + tile * kBI;
+    const int first = sFirst[tile];
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int p = k / C::CPT, j = k % C::CPT;
-      const int r = p * C::RPP + srow, u = sch + C::TPR * j;
-      chunk_t v{};
-      if ((kBI % C::RPP == 0 || r < kBI) && (C::CPR % C::TPR == 0 || u < C::CPR)) {
-        // invalid slots hold -1 - (a valid row of the tile): load that row
-        // (finite data; the slot's score is masked and its p is exactly 0)
-        int row = ti[r];
-        row = row >= 0 ? row : -1 - row;
-        v = *reinterpret_cast<const chunk_t*>(kvb + (size_t)row * DQK + C::TPR * j * 8);
-      }
-      pre[k] = v;
+    for (int p = 0; p < C::PASSES; ++p) {
+      const int r = p * C::RPP + srow;
+      const int row = (kBI % C::RPP == 0 || r < kBI) ? ti[r] : 0;
+      grow[p] = row >= 0 ? row : first;
     }
     if constexpr (FP8) {
       if (tid < kBI) {
@@ -259,32 +313,60 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       }
     }
   };
-  auto lstore = [&](uint16_t* dst, float* dsc) {
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int p = k / C::CPT, j = k % C::CPT;
-      const int r = p * C::RPP + srow, u = sch + C::TPR * j;
-      if ((kBI % C::RPP == 0 || r < kBI) && (C::CPR % C::TPR == 0 || u < C::CPR)) {
-        i32x4 v;
-        if constexpr (FP8) {
-          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-          const uint2 raw = pre[k];
-          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
-          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
-          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
-          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
-          v = i32x4{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1),
-                    __builtin_bit_cast(int, p2), __builtin_bit_cast(int, p3)};
-        } else {
-          v = pre[k];
-        }
-        *reinterpret_cast<i32x4*>(dst + r * C::RS + u * 8) = v;
-      }
+  auto gather_chunk = [&](int k) {
+    chunk_t v{};
+    if (chunk_ok(k))
+      v = *reinterpret_cast<const chunk_t*>(kvb + (size_t)grow[k / C::CPT] * DQK +
+                                            C::TPR * (k % C::CPT) * 8);
+    pre[k] = v;
+  };
+  auto store_chunk = [&](uint16_t* dst, int k) {
+    if (!chunk_ok(k)) return;
+    const int r = (k / C::CPT) * C::RPP + srow, u = sch + C::TPR * (k % C::CPT);
+    i32x4 v;
+    if constexpr (FP8) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const uint2 raw = pre[k];
+      const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
+      const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
+      const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
+      const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
+      v = i32x4{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1),
+                __builtin_bit_cast(int, p2), __builtin_bit_cast(int, p3)};
+    } else {
+      v = pre[k];
     }
+    *reinterpret_cast<i32x4*>(dst + r * C::RS + u * 8) = v;
+  };
+  auto store_scale = [&](float* dsc) {
     if constexpr (FP8) {
       if (tid < kBI) dsc[tid] = pscale;
     }
   };
+  auto gload = [&](int tile) {
+    gather_rows(tile);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) gather_chunk(k);
+  };
+  auto lstore = [&](uint16_t* dst, float* dsc) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) store_chunk(dst, k);
+    store_scale(dsc);
+  };
+  // Staging schedule (at most half the chunks in registers at a time): the
+  // first GH chunks are loaded over the first half of the QK^T k-steps and
+  // written to LDS over the second half (the other buffer is free since the
+  // barrier that started this tile); the others are loaded over the second
+  // half and written during the first half of PV, so that the stores have
+  // drained by the next barrier.
+  constexpr int GH = (NC + 1) / 2, QH = C::QC / 2;
+  // QK^T k-step after which chunk k is loaded
+  auto gstep = [](int k) {
+    return k < GH ? (k * QH) / GH : QH + ((k - GH) * (C::QC - QH)) / (NC - GH);
+  };
+  // QK^T k-step after which chunk k is stored (chunks k < GH), PV column step (others)
+  auto sqk = [](int k) { return QH + (k * (C::QC - QH)) / GH; };
+  auto spv = [](int k) { return ((k - GH) * ((OTW + 1) / 2)) / (NC - GH > 0 ? NC - GH : 1); };
 
   // ---- one tile: S^T = KV.Q^T, softmax, O^T += V^T.P^T -----------------------
   // MFMA tile tau covers gathered rows 16*tau .. 16*tau+15 (A-row r = row
@@ -294,7 +376,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   // transposing reads of the 4-row blocks at rows 4g and 16+4g.
   // mode 0: reference = max of the first tile; 1: max-only pre-pass;
   // 2: reference = exact max from the pre-pass.  P goes to LDS (sP).
-  auto qk_softmax = [&](const uint16_t* sK, const float* sS, int tile, int it, int mode) {
+  // With `gat`, the gather chunks of the tile whose rows are in grow are
+  // loaded between the k-steps, and the first GH of them stored to dst.
+  // This wave's own P fragments stay in pown.
+  bf16x8 pown[HT];
+  auto qk_softmax = [&](const uint16_t* sK, const float* sS, int tile, int it, int mode,
+                        bool gat, uint16_t* dst) {
     f32x4 s[2][HT];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
@@ -308,11 +395,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       const uint16_t* a0 = sK + col * C::RS + g * 8;
       const uint16_t* a1 = a0 + 16 * C::RS;
       constexpr int R = kLA + 1;
-      bf16x8 xa[R][2], xq[R];
+      bf16x8 xa[R][2], xq[R][HT];
       auto ld = [&](int c) {
         xa[c % R][0] = *reinterpret_cast<const bf16x8*>(a0 + c * 32);
         xa[c % R][1] = *reinterpret_cast<const bf16x8*>(a1 + c * 32);
-        if (c >= C::QR) xq[c % R] = sQ[c - C::QR][wave][lane];
+        if (c >= C::QR) {
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) xq[c % R][ht] = sQ[c - C::QR][wave][ht][lane];
+        }
       };
 #pragma unroll
       for (int c = 0; c < kLA && c < C::QC; ++c) ld(c);
@@ -321,30 +411,35 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         if (c + kLA < C::QC) ld(c + kLA);
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-          const bf16x8 qb = c < C::QR ? qf[ht][c < C::QR ? c : 0] : xq[c % R];
-          s[0][ht] = mfma_bf16_16x16x32(xa[c % R][0], qb, s[0][ht]);
-          s[1][ht] = mfma_bf16_16x16x32(xa[c % R][1], qb, s[1][ht]);
+          const bf16x8 qb = c < C::QR ? qf[ht][c < C::QR ? c : 0] : xq[c % R][ht];
+          qk_mfma(s[0][ht], xa[c % R][0], qb);
+          qk_mfma(s[1][ht], xa[c % R][1], qb);
+        }
+        if (gat) {
+#pragma unroll
+          for (int k = 0; k < GH; ++k)
+            if (sqk(k) == c) store_chunk(dst, k);
+#pragma unroll
+          for (int k = 0; k < NC; ++k)
+            if (gstep(k) == c) gather_chunk(k);
         }
         if (kSchedBarrier) __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) qk_drain(s[0][ht], s[1][ht]);
     }
     // tv = score * sm_scale * log2(e) - reference (log2 units), -inf when masked
     float tv[HT][8];
-    bool over = false;
     if ((mode == 2 || (mode == 0 && it > 0)) && sFull[tile]) {
       // steady state on a tile whose 32 indices are all valid: no masking
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        float mx = -INFINITY;
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int jj = (i < 4 ? 0 : 16) + (i & 3);
           const float scl = FP8 ? sS[jj + 4 * g] * scale_log2 : scale_log2;
           tv[ht][i] = fmaf(s[i >> 2][ht][i & 3], scl, -m[ht]);
-          mx = fmaxf(mx, tv[ht][i]);
         }
-        over = over || (mode == 0 && mx > kRefSlack);
-      }
     } else {
       const int* ti = sIdx + tile * kBI + 4 * g;
 #pragma unroll
@@ -365,15 +460,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
           mx = fmaxf(mx, wave_xor(mx, 32));
           // the first tile holds a valid index, so every head's max is finite
           m[ht] = mode == 1 ? fmaxf(m[ht], mx) : mx;
-        } else if (mode == 0) {
-          over = over || (mx > m[ht] + kRefSlack);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) tv[ht][i] = sv[i] - m[ht];
       }
     }
     if (mode == 1) return;
-    if (__ballot(over) != 0ull && lane == 0) sFlag[it & 1] = 1;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       float psum = 0.f;
@@ -389,80 +481,108 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         pk[i >> 1] = pack_bf16x2(p0, p1);
       }
       lsum[ht] += psum;
-      sP[wave][ht][lane] =
-          __builtin_bit_cast(bf16x8, i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
+      pown[ht] = __builtin_bit_cast(bf16x8, i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
+      if constexpr (PG > 1) sP[wave][ht][lane] = pown[ht];
     }
   };
-  // PV of a tile whose P fragments are in sP: this wave's own, or those of
-  // its whole P group.
-  auto pv_tile = [&](const uint16_t* sK) {
+  // PV of a tile: O^T += V^T P^T over this wave's heads (PG = 1), or over
+  // the whole P group's heads for this wave's Dv/PG columns.  O tile oh
+  // belongs to the group's wave (wave + oh/HT) % PG, head tile oh % HT: the
+  // first HT are this wave's own, whose P is still in registers, so the
+  // first MFMAs need no LDS read.  The staged chunks go to dst between the
+  // column steps.  The first kLA V fragments are read by pv_prefetch, which
+  // can run before the barrier that publishes P.
+  auto pgrp = [&](int oh) { return (wave % PG + oh / HT) % PG; };
+  // A operand: lane (c = c0 + 16t + col, g) needs V[4g..4g+3][c] and
+  // V[16+4g..16+4g+3][c]: two transposing reads.
+  const int voff = (4 * g + (col >> 2)) * C::RS + ((col & 3) >> 1) * 8 + 4 * (col & 1) + c0;
+  auto vload = [&](const uint16_t* sK, int t) {
+    const i16x4 lo = lds_read_tr16(sK + voff + t * 16);
+    const i16x4 hi = lds_read_tr16(sK + voff + 16 * C::RS + t * 16);
+    return __builtin_bit_cast(bf16x8,
+                              i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  constexpr int RV = kLA + 1;
+  bf16x8 va[RV];
+  auto pv_prefetch = [&](const uint16_t* sK) {
+#pragma unroll
+    for (int t = 0; t < kLA && t < OTW; ++t) va[t % RV] = vload(sK, t);
+  };
+  auto pv_tile = [&](const uint16_t* sK, uint16_t* dst) {
     bf16x8 pv[OH];
-    if constexpr (PG > 1) {
 #pragma unroll
-      for (int k = 0; k < PG; ++k) pv[k] = sP[(wave / PG) * PG + k][0][lane];
-    } else {
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) pv[ht] = sP[wave][ht][lane];
-    }
-    // A operand: lane (c = c0 + 16t + col, g) needs V[4g..4g+3][c] and
-    // V[16+4g..16+4g+3][c]: two transposing reads.
-    const int vr = 4 * g + (col >> 2);  // and vr + 16
-    const uint16_t* vb =
-        sK + vr * C::RS + ((col & 3) >> 1) * 8 + 4 * (col & 1) + c0;
-    auto vload = [&](int t) {
-      const i16x4 lo = lds_read_tr16(vb + t * 16);
-      const i16x4 hi = lds_read_tr16(vb + 16 * C::RS + t * 16);
-      return __builtin_bit_cast(bf16x8,
-                                i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-    };
-    constexpr int R = kLA + 1;
-    bf16x8 va[R];
-#pragma unroll
-    for (int t = 0; t < kLA && t < OTW; ++t) va[t % R] = vload(t);
+    for (int oh = 0; oh < OH; ++oh)
+      pv[oh] = oh < HT ? pown[oh % HT] : sP[(wave / PG) * PG + pgrp(oh)][oh % HT][lane];
 #pragma unroll
     for (int t = 0; t < OTW; ++t) {
-      if (t + kLA < OTW) va[(t + kLA) % R] = vload(t + kLA);
+      if (t + kLA < OTW) va[(t + kLA) % RV] = vload(sK, t + kLA);
 #pragma unroll
       for (int oh = 0; oh < OH; ++oh)
-        oacc[oh][t] = mfma_bf16_16x16x32(va[t % R], pv[oh], oacc[oh][t]);
+        oacc[oh][t] = mfma_bf16_16x16x32(va[t % RV], pv[oh], oacc[oh][t]);
+#pragma unroll
+      for (int k = GH; k < NC; ++k)
+        if (spv(k) == t) store_chunk(dst, k);
       if (kSchedBarrier) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Tile schedule.  Iteration `it`: QK^T + softmax of tile it | barrier |
-  // load this thread's share of tile it+1 into VGPRs, PV of tile it, write
-  // the share to LDS (the other buffer, last read in iteration it-1).
+  // Tile schedule.  Iteration `it`: QK^T + softmax of tile it, with this
+  // thread's share of tile it+1 loaded into VGPRs in between; the first V
+  // fragments of tile it | barrier | PV of tile it, with the share written
+  // to the other LDS buffer (last read in iteration it-1) in between.  The
+  // last iteration re-gathers its own tile (L2-warm, never read) so that the
+  // loop body has no branches.
+  //
+  // With the reference fixed at the first tile's max, p = 2^(s - ref) grows
+  // past 1 when a later score exceeds it; bf16 P and fp32 O and l represent
+  // that exactly as long as nothing overflows, so the check is made once, at
+  // the end: a head whose partial sum passed 2^40 (every p <= 2^40, far from
+  // the fp32 range) restarts the token with a max-only pre-pass and a final
+  // pass at the exact max.
 #pragma unroll 1
   for (int mode = 0;;) {
-    if (tid < 2) sFlag[tid] = 0;
+    if (tid == 0) sFlag[0] = 0;
     if (nvt > 0) {
       gload(sList[0]);
       lstore(sKV[0], sSc[0]);
     }
-    bool restart = false;
 #pragma unroll 1
     for (int it = 0; it < nvt; ++it) {
       const uint16_t* cur = sKV[it & 1];
       uint16_t* nxt = sKV[(it + 1) & 1];
       const float* curS = sSc[it & 1];
       float* nxtS = sSc[(it + 1) & 1];
-      __syncthreads();  // tile it complete; flags of tile it-1 final
-      if (it > 0 && sFlag[(it - 1) & 1]) {  // uniform
-        restart = true;
-        break;
-      }
+      __syncthreads();  // tile it complete
       const bool more = it + 1 < nvt;
-      const int ntile = more ? sList[it + 1] : 0;
-      qk_softmax(cur, curS, sList[it], it, mode);
+      gather_rows(sList[more ? it + 1 : it]);
+      qk_softmax(cur, curS, sList[it], it, mode, true, nxt);
+      pv_prefetch(cur);
       __syncthreads();  // P of the whole P group visible
-      // slot of tile it+1; it last held tile it-1's flag, checked above
-      if (tid == ((it + 1) & 1)) sFlag[tid] = 0;
-      if (more) gload(ntile);
-      if (mode != 1) pv_tile(cur);
-      if (more) lstore(nxt, nxtS);
+      // (in the max-only pre-pass P is stale and O is discarded; PV still
+      // runs, for the staging stores between its steps)
+      pv_tile(cur, nxt);
+      store_scale(nxtS);
+    }
+    if (mode == 0) {
+      bool bad = false;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) bad = bad || !(lsum[ht] <= kPLimit);
+      if (__ballot(bad) != 0ull && lane == 0) sFlag[0] = 1;
+    }
+    // l and m of each head to the P group (read after the final pass)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float l = lsum[ht];
+      l += wave_xor(l, 16);
+      l += wave_xor(l, 32);
+      lsum[ht] = l;
+      if (PG > 1 && g == 0) {
+        sL[PG > 1 ? wave : 0][ht][col] = l;
+        sM[PG > 1 ? wave : 0][ht][col] = m[ht];
+      }
     }
     __syncthreads();
-    restart = restart || sFlag[0] || sFlag[1];
+    const bool restart = sFlag[0] != 0;
     if (mode == 1 || restart) {
       // pre-pass done -> final pass; or restart: pre-pass from scratch
       mode = mode == 1 ? 2 : 1;
@@ -484,56 +604,77 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   // ---- sink, normalise, store ------------------------------------------------
   // l and m of the heads of this wave's O tiles (P groups: exchanged via LDS)
   float lf[OH], mf[OH];
+  if constexpr (PG == 1) {
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    float l = lsum[ht];
-    l += wave_xor(l, 16);
-    l += wave_xor(l, 32);
-    if constexpr (PG > 1) {
-      if (g == 0) {
-        sL[wave][col] = l;
-        sM[wave][col] = m[ht];
-      }
-    } else {
-      lf[ht] = l;
+    for (int ht = 0; ht < HT; ++ht) {
+      lf[ht] = lsum[ht];
       mf[ht] = m[ht];
     }
-  }
-  if constexpr (PG > 1) {
-    __syncthreads();
+  } else {
 #pragma unroll
-    for (int k = 0; k < PG; ++k) {
-      lf[k] = sL[(wave / PG) * PG + k][col];
-      mf[k] = sM[(wave / PG) * PG + k][col];
+    for (int oh = 0; oh < OH; ++oh) {
+      lf[oh] = sL[(wave / PG) * PG + pgrp(oh)][oh % HT][col];
+      mf[oh] = sM[(wave / PG) * PG + pgrp(oh)][oh % HT][col];
     }
   }
-  if (wso) {
+  if constexpr (SPLIT) {
     // split: unnormalised O, and (m, l) of each head, for the merge kernel
     const size_t part = (size_t)rtok * S + split;
 #pragma unroll
     for (int oh = 0; oh < OH; ++oh) {
-      const int h = PG > 1 ? (wave / PG) * PG * 16 + oh * 16 + col : h0 + 16 * oh;
+      const int h = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 + col;
       float* orow = wso + (part * Hq + h) * DV + c0 + g * 4;
 #pragma unroll
       for (int t = 0; t < OTW; ++t) *reinterpret_cast<f32x4*>(orow + t * 16) = oacc[oh][t];
       if (g == 0 && wave % PG == 0) wsml[part * Hq + h] = float2{mf[oh], lf[oh]};
     }
-    return;
-  }
+  } else {
+    // Normalised bf16 O goes through LDS (the KV tile buffers, free now) in
+    // OP passes over the heads, so that every head row of o is written whole
+    // with 16-byte lanes: stored straight from the MFMA layout, each store
+    // instruction would write 16 separate 32-byte pieces.  Row stride OS =
+    // DV + 8 elements keeps the 8-byte LDS writes of 32 lanes on distinct
+    // banks.  The lane's position is recomputed here rather than kept live
+    // (and spilled) across the tile loop.
+    constexpr int OS = DV + 8;
+    constexpr int OP = (NW * HPW * OS * 2 + (int)sizeof(sKV) - 1) / (int)sizeof(sKV);
+    constexpr int ORP = NW * HPW / OP;  // head rows per pass
+    static_assert((NW * HPW) % OP == 0 && ORP * OS * 2 <= (int)sizeof(sKV), "O staging");
+    uint16_t* so = &sKV[0][0];
+    const int ln = fresh_lane_id(), colx = ln & 15, gx = ln >> 4;
+    float inv[OH];
 #pragma unroll
-  for (int oh = 0; oh < OH; ++oh) {
-    const int h = PG > 1 ? (wave / PG) * PG * 16 + oh * 16 + col : h0 + 16 * oh;
-    float l = lf[oh];
-    if (sink) l += fast_exp2(sink[h] * kLog2e - mf[oh]);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = o + ((size_t)rtok * Hq + h) * DV + c0 + g * 4;
+    for (int oh = 0; oh < OH; ++oh) {
+      const int h = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 + colx;
+      float l = lf[oh];
+      if (sink) l += fast_exp2(sSink[h] * kLog2e - mf[oh]);
+      inv[oh] = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+    }
 #pragma unroll
-    for (int t = 0; t < OTW; ++t) {
-      const f32x4 v = oacc[oh][t] * inv;
-      uint2 pk2;
-      pk2.x = pack_bf16x2(v[0], v[1]);
-      pk2.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(orow + t * 16) = pk2;
+    for (int pass = 0; pass < OP; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's rows are read
+#pragma unroll
+      for (int oh = 0; oh < OH; ++oh) {
+        const int hr = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 - pass * ORP;
+        if (hr >= 0 && hr < ORP) {  // uniform over the wave
+          uint16_t* srow = so + (hr + colx) * OS + c0 + gx * 4;
+#pragma unroll
+          for (int t = 0; t < OTW; ++t) {
+            const f32x4 v = oacc[oh][t] * inv[oh];
+            uint2 pk2;
+            pk2.x = pack_bf16x2(v[0], v[1]);
+            pk2.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(srow + t * 16) = pk2;
+          }
+        }
+      }
+      __syncthreads();
+      uint16_t* obase = o + ((size_t)rtok * Hq + pass * ORP) * DV;
+      for (int u = tid; u < ORP * (DV / 8); u += C::THREADS) {
+        const int r = u / (DV / 8), c8 = u % (DV / 8);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * DV + c8 * 8) =
+            *reinterpret_cast<const i32x4*>(so + r * OS + c8 * 8);
+      }
     }
   }
 }
@@ -616,10 +757,17 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   }
   float* wso = static_cast<float*>(ws);
   float2* wsml = ws ? reinterpret_cast<float2*>(wso + (size_t)rows * S * a.Hq * DV) : nullptr;
-  hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW>), dim3((unsigned)(rows * S)),
-                     dim3(C::THREADS), 0, stream, (const uint16_t*)a.q, a.kv, a.kv_scale,
-                     a.attn_sink, a.topk_idxs, (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K,
-                     scale_log2, S, kspan, wso, wsml);
+  if (ws)
+    hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, true>),
+                       dim3((unsigned)(rows * S)), dim3(C::THREADS), 0, stream,
+                       (const uint16_t*)a.q, a.kv, a.kv_scale, a.attn_sink, a.topk_idxs,
+                       (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K, scale_log2, S, kspan, wso,
+                       wsml);
+  else
+    hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, false>), dim3((unsigned)rows),
+                       dim3(C::THREADS), 0, stream, (const uint16_t*)a.q, a.kv, a.kv_scale,
+                       a.attn_sink, a.topk_idxs, (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K,
+                       scale_log2, 1, a.K, nullptr, nullptr);
   hipError_t err = hipGetLastError();
   if (ws) {
     if (err == hipSuccess) {
@@ -636,7 +784,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
 
 // Heads per wave at 128 heads (tuning knob: 32 -> 4 waves, 16 -> 8 waves).
 #ifndef DSA_ATTN_HPW128
-#define DSA_ATTN_HPW128 16
+#define DSA_ATTN_HPW128 32
 #endif
 
 template <int DQK, int DV, bool FP8>

@@ -113,22 +113,27 @@ def test_attn_workloads(name):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("where", ["middle", "last", "first"])
+@pytest.mark.parametrize("where", ["middle", "last", "first", "moderate"])
 def test_attn_reference_restart(fp8, where):
     """A score far above every score of the first tile (the kernel's fixed
-    softmax reference) forces the max-only pre-pass and the second pass."""
+    softmax reference: 72 natural units, p ~ 2^104) forces the max-only
+    pre-pass and the second pass.  "moderate": ~21 natural units above (p ~
+    2^30), which the fixed reference carries exactly without a restart."""
     B, M, N, K = 1, 2, 600, 256
     wl = W.Workload("r", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, kv_fp8=fp8,
                     seed=6)
     x = W.make_inputs(wl, parts=("attn",))
-    big = {"middle": 300, "last": 599, "first": 3}[where]
+    big = {"middle": 300, "last": 599, "first": 3, "moderate": 300}[where]
     qv = torch.ones((B, M, wl.Hq, wl.Dqk), dtype=torch.float32) * 0.5
     qv[..., ::2] = 1.0
     x["q"] = qv.to(torch.bfloat16)
     kvf = torch.from_numpy(np.random.default_rng(1).standard_normal((B, N, wl.Dqk))
                            .astype(np.float32))
-    kvf[0, big] = 4.0          # q.k/24 = 72 (natural units) above the others
-    kvf[0, big, :8] = -3.0
+    if where == "moderate":
+        kvf[0, big] = 1.25     # q.k/24 = 22.5; o ~ 1.25, exact in bf16
+    else:
+        kvf[0, big] = 4.0      # q.k/24 = 72 (natural units) above the others
+        kvf[0, big, :8] = -3.0
     if fp8:
         x["kv"], x["kv_scale"] = W.quantize_e4m3fn_rows(kvf.numpy())
     else:
