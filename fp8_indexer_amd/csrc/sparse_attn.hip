@@ -77,6 +77,9 @@ constexpr int kPG = DSA_ATTN_PG;
 #ifndef DSA_ATTN_QL32
 #define DSA_ATTN_QL32 5
 #endif
+#ifndef DSA_ATTN_SQKEND
+#define DSA_ATTN_SQKEND 0
+#endif
 constexpr bool kSchedBarrier = DSA_ATTN_SB != 0;
 
 template <int DQK, int DV, bool FP8, int NW, int HPW>
@@ -364,8 +367,10 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   auto gstep = [](int k) {
     return k < GH ? (k * QH) / GH : QH + ((k - GH) * (C::QC - QH)) / (NC - GH);
   };
-  // QK^T k-step after which chunk k is stored (chunks k < GH), PV column step (others)
-  auto sqk = [](int k) { return QH + (k * (C::QC - QH)) / GH; };
+  // QK^T k-step after which chunk k is stored (chunks k < GH; QC: after the
+  // last k-step, beside the softmax, whose VALU work leaves LDS idle), PV
+  // column step (others)
+  auto sqk = [](int k) { return DSA_ATTN_SQKEND ? C::QC : QH + (k * (C::QC - QH)) / GH; };
   auto spv = [](int k) { return ((k - GH) * ((OTW + 1) / 2)) / (NC - GH > 0 ? NC - GH : 1); };
 
   // ---- one tile: S^T = KV.Q^T, softmax, O^T += V^T.P^T -----------------------
@@ -427,6 +432,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) qk_drain(s[0][ht], s[1][ht]);
+      if (gat) {
+#pragma unroll
+        for (int k = 0; k < GH; ++k)
+          if (sqk(k) == C::QC) store_chunk(dst, k);
+      }
     }
     // tv = score * sm_scale * log2(e) - reference (log2 units), -inf when masked
     float tv[HT][8];

@@ -17,12 +17,15 @@
 // (K - #above) keys == tau, at their ascending output slot.  No atomics touch
 // the output, so it is deterministic.
 //
-// Rows of up to 8192 keys (N <= 8192): one 256-thread workgroup per row,
+// Rows whose window has up to 8192 keys: one 256-thread workgroup per row,
 // each wave holding a contiguous quarter of the row in VGPRs (digits of 11,
-// 11 and 10 bits, a shared LDS histogram, wave-level scans).  Longer rows:
-// one 512-thread workgroup per row, 16 keys per lane in VGPRs up to 8192
-// keys and re-read from L2 on each pass beyond (digits 12, 10, 10).  Rows
-// with len <= K only write s..e-1 and -1 padding.
+// 11 and 10 bits, a shared LDS histogram, wave-level scans).  The path is
+// chosen per row from its own window, not from N: longer windows (only
+// possible when N > 8192) are left to a second launch, which cuts them into
+// 8192-key segments and reduces the segments' candidates, or, when that
+// launch's candidate buffer would be large, gives each row one 512-thread
+// workgroup that re-reads the row from L2 on each pass (digits 12, 10, 10).
+// Rows with len <= K only write s..e-1 and -1 padding.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -68,7 +71,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int& total, int* sWave) {
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ logits,
                                                           const int* __restrict__ ks,
                                                           const int* __restrict__ ke,
-                                                          int* __restrict__ out, int N, int K) {
+                                                          int* __restrict__ out, int N, int K,
+                                                          int skip_len) {
   __shared__ uint32_t hist[4096];
   __shared__ int sWave[kTkWaves];
   __shared__ int sCnt[2][kTkWaves];
@@ -80,6 +84,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   const int e = clampi(ke[r], s, N);
   const int len = e - s;
   int* o = out + r * (size_t)K;
+  if (skip_len > 0 && len <= skip_len) return;  // done by the row kernel
 
   if (len <= K) {  // short row: the whole window, then -1 padding
     for (int i = tid; i < K; i += kTkThreads) o[i] = i < len ? s + i : -1;
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
     return;
   }
+  if (len > kRowThreads * KR) return;  // a long row: the long-row kernels take it
   row_select<KR, false>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel, sCnt);
 }
 
@@ -396,14 +402,16 @@ __global__ __launch_bounds__(kRowThreads) void topk_seg_kernel(const float* __re
                                                                const int* __restrict__ ks,
                                                                const int* __restrict__ ke,
                                                                int* __restrict__ cand, int N, int K,
-                                                               int nseg) {
+                                                               int nseg, int skip_len) {
   DSA_TOPK_LDS
   const int tid = threadIdx.x;
   const size_t r = blockIdx.x / nseg;
   const int seg = (int)(blockIdx.x % nseg);
   const int s = clampi(ks[r], 0, N);
   const int e = clampi(ke[r], s, N);
-  if (e - s <= K) return;  // level 2 writes short rows directly
+  // level 2 writes rows of at most K keys directly; rows of at most
+  // skip_len keys are the row kernel's
+  if (e - s <= K || e - s <= skip_len) return;
   const int s0 = s + seg * kSegKeys;
   const int len = min(e - s0, kSegKeys);
   if (len <= 0) return;
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __
                                                                  const int* __restrict__ ke,
                                                                  const int* __restrict__ cand,
                                                                  int* __restrict__ out, int N, int K,
-                                                                 int nseg) {
+                                                                 int nseg, int skip_len) {
   DSA_TOPK_LDS
   const int tid = threadIdx.x;
   const size_t r = blockIdx.x;
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __
   const int e = clampi(ke[r], s, N);
   const int len = e - s;
   int* o = out + r * (size_t)K;
+  if (skip_len > 0 && len <= skip_len) return;  // done by the row kernel
   if (len <= K) {
     for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
     return;
@@ -450,42 +459,56 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const long long rows = a.B * a.M;
   if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-  // rows of up to 8192 keys: kRowWaves waves per row, keys in VGPRs
+  // Rows of up to 8192 keys: kRowWaves waves per row, keys in VGPRs.  The
+  // path is chosen per row from its own window: with N > 8192 the row
+  // kernel still takes every row of up to 8192 keys, and the long-row
+  // kernels that follow skip those rows.
   if (a.N <= kRowThreads * (4096 / kRowThreads)) {
     hipLaunchKernelGGL(topk_row_kernel<4096 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
                        a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
-  if (a.N <= kRowThreads * (8192 / kRowThreads)) {
-    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
-                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
-    return hipGetLastError();
-  }
-  // longer rows: two levels through a stream-ordered candidate buffer while
-  // the candidates of a row fit one workgroup's registers
   const int nseg = (int)((a.N + kSegKeys - 1) / kSegKeys);
   const long long ncand = (long long)nseg * a.K;
-  if (a.K <= kSegKeys && ncand <= kRowThreads * 64 && rows * nseg <= 0x7fffffffLL) {
+  const size_t ws_bytes = (size_t)rows * ncand * sizeof(int);
+  const bool two_level = a.N > kSegKeys && a.K <= kSegKeys && ncand <= kRowThreads * 64 &&
+                         rows * nseg <= 0x7fffffffLL && ws_bytes <= ((size_t)256 << 20);
+  // With few rows (decode) and two levels, the two-level kernels take every
+  // row, as one more launch would cost more than the short rows gain.
+  const bool rows_first = !(two_level && rows < 256);
+  const int skip_len = rows_first ? kRowThreads * (8192 / kRowThreads) : 0;
+  hipError_t err = hipSuccess;
+  if (rows_first) {
+    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
+                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+    err = hipGetLastError();
+    if (err != hipSuccess || a.N <= kRowThreads * (8192 / kRowThreads)) return err;
+  }
+  // Longer rows: two levels through a stream-ordered candidate buffer while
+  // the candidates of a row fit one workgroup's registers and the buffer
+  // (sized for every row, since the host does not know which rows are long)
+  // stays modest; else one streaming workgroup per row.
+  if (two_level) {
     keep_pool_memory();
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, (size_t)rows * ncand * sizeof(int), stream) == hipSuccess) {
+    if (hipMallocAsync(&ws, ws_bytes, stream) == hipSuccess) {
       int* cand = static_cast<int*>(ws);
       hipLaunchKernelGGL(topk_seg_kernel, dim3((unsigned)(rows * nseg)), dim3(kRowThreads), 0,
-                         stream, a.logits, a.ks, a.ke, cand, (int)a.N, (int)a.K, nseg);
-      hipError_t err = hipGetLastError();
+                         stream, a.logits, a.ks, a.ke, cand, (int)a.N, (int)a.K, nseg, skip_len);
+      err = hipGetLastError();
       if (err == hipSuccess) {
         if (ncand <= kRowThreads * 16)
           hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)rows), dim3(kRowThreads), 0,
                              stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg);
+                             nseg, skip_len);
         else if (ncand <= kRowThreads * 32)
           hipLaunchKernelGGL(topk_merge_kernel<32>, dim3((unsigned)rows), dim3(kRowThreads), 0,
                              stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg);
+                             nseg, skip_len);
         else
           hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)rows), dim3(kRowThreads), 0,
                              stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg);
+                             nseg, skip_len);
         err = hipGetLastError();
       }
       const hipError_t ferr = hipFreeAsync(ws, stream);
@@ -494,7 +517,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     (void)hipGetLastError();
   }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a.logits,
-                     a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+                     a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K, skip_len);
   return hipGetLastError();
 }
 

@@ -116,9 +116,37 @@ def test_topk_two_level_rows(kind, K):
     """N in (8192, 65536]: long rows are cut into 8192-key segments whose
     top-K candidates are then reduced; lengths straddle segment boundaries."""
     rng = np.random.default_rng(K + len(kind))
-    B, M, N = 1, 8, 40000
+    B, M, N = 1, 10, 40000
     lg = _dist(kind, (B, M, N), rng)
-    ks = np.array([[0, 0, 0, 0, 0, 100, 31000, 5]], np.int32)
-    ke = np.array([[N, K + 1, 8192, 8193, 16384 + 7, 24000, N, 5 + K]], np.int32)
+    # ... plus an empty row and a row shorter than K (written as -1 padded)
+    ks = np.array([[0, 0, 0, 0, 0, 100, 31000, 5, 7, 0]], np.int32)
+    ke = np.array([[N, K + 1, 8192, 8193, 16384 + 7, 24000, N, 5 + K, 7, K - 1]], np.int32)
     log(f"topk two-level {kind} K={K}")
     _compare(lg, ks, ke, K, what=f"two-level {kind}/K{K}")
+
+
+def test_topk_many_long_rows_streaming():
+    """N > 8192 with more rows than the two-level candidate buffer allows
+    (rows * ceil(N / 8192) * K * 4 bytes > 256 MiB): rows of up to 8192 keys
+    go to the register-resident kernel, longer ones to one streaming
+    workgroup each.  Sampled rows include every long row."""
+    B, M, N, K = 1, 17000, 16384, 2048
+    rng = np.random.default_rng(23)
+    ks = rng.integers(0, 4000, (B, M)).astype(np.int32)
+    ke = (ks + rng.integers(0, 8193, (B, M))).astype(np.int32)
+    long_rows = np.array([3, 777, 8000, 16999])
+    ks[0, long_rows] = [0, 5, 100, 0]
+    ke[0, long_rows] = [N, 16000, 8293, 8193]
+    log("topk many long rows (streaming)")
+    gen = torch.Generator().manual_seed(5)
+    lg = torch.randn((B, M, N), generator=gen, dtype=torch.float32)
+    lg[0, :100] = torch.round(lg[0, :100] * 2) / 2  # some tie-heavy rows
+    out = dsa.topk(lg.to("cuda"), dev(ks), dev(ke), K)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().reshape(M, K)
+    rows = np.unique(np.concatenate([sample_rows(M, 60, seed=4, must=[0, 1, 50, M - 1]),
+                                     long_rows]))
+    flat = lg.numpy().reshape(M, N)
+    ref = oracle.topk(flat[rows], ks, ke, B, M, N, K, rows=rows)
+    bad = np.nonzero(~np.all(g[rows] == ref, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first row {rows[bad[0]]}"
