@@ -37,9 +37,17 @@ constexpr int kIdxWaves = DSA_IDX_WAVES;
 constexpr int kIdxThreads = kIdxWaves * kWave;
 constexpr int kRowsPerWave = 128;               // (token, head) rows per wave
 constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
-constexpr int kKT = 64;                         // keys per LDS tile
+#ifndef DSA_IDX_KT
+#define DSA_IDX_KT 64
+#endif
+constexpr int kKT = DSA_IDX_KT;                 // keys per LDS tile (tuning knob)
 constexpr int kXcds = 8;
 constexpr int kMinChunk = 512;  // keys per chunk, at least
+// VALU instructions scheduled after each MFMA of the next sub-tile (tuning knob)
+#ifndef DSA_IDX_VPM
+#define DSA_IDX_VPM 10
+#endif
+constexpr int kIdxVpm = DSA_IDX_VPM;
 
 // KP (key-parallel, for decode-like inputs with at most TW tokens per batch
 // entry): all waves of a workgroup hold the same tokens and each takes one
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   // before the window reduction, which they do not depend on) ------------
   const int tw0 = KP ? t0 : t0 + wave * C::TW;
   i32x8 qf[kRT][C::KS];
-  float weff[kRT][4];
+  float weff[kRT][4], qsc[kRT][4];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     // A row col of tile rt is C row (g', i') = (col / 4, col % 4)
@@ -176,12 +184,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     for (int i = 0; i < 4; ++i) {
       const int L2 = 32 * g + 4 * rt + i;
       const int t2 = tw0 + L2 / H, h2 = L2 % H;
-      float we = 0.f;
+      float we = 0.f, qs = 1.f;
       if (t2 < M) {
         const size_t o = (size_t)(b * M + t2) * H + h2;
-        we = w[o] * (q_scale ? q_scale[o] : 1.f);
+        we = w[o];
+        if (q_scale) qs = q_scale[o];
       }
-      weff[rt][i] = we;
+      weff[rt][i] = we;  // times qsc once the loads are in (below)
+      qsc[rt][i] = qs;
     }
   }
   // ---- window union of the block: [kmin, kmax) ---------------------------
@@ -249,11 +259,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   // a lane stores the sums of its tokens if it is the first of their groups
   const bool store_lane = (g % C::GPT) == 0;
 
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) weff[rt][i] *= qsc[rt][i];
+
   // ---- K tile staging -----------------------------------------------------
+  // Two register sets: the loads of tile t+2 are issued while tile t is
+  // computed and stored to LDS at the end of tile t+1, so each load has two
+  // tiles of compute to arrive.
   const int ntiles = (c1 - c0 + C::KT - 1) / C::KT;
-  i32x4 pre[C::CPT];
-  float pks = 0.f;
-  auto gload = [&](int tile) {
+  i32x4 pre2[2][C::CPT];
+  float pks2[2] = {0.f, 0.f};
+  // register set / LDS buffer of tile t: t & 1, a compile-time SETC below
+  auto gload = [&](int tile, auto setc) {
+    constexpr int SET = decltype(setc)::value;
+    i32x4* pre = pre2[SET];
+    float& pks = pks2[SET];
     const int kb = c0 + tile * C::KT;
 #pragma unroll
     for (int j = 0; j < C::CPT; ++j) {
@@ -271,7 +293,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       pks = key < c1 ? k_scale[(size_t)b * N + key] : 0.f;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](auto setc) {
+    constexpr int SET = decltype(setc)::value;
+    constexpr int buf = SET;
+    const i32x4* pre = pre2[SET];
+    const float pks = pks2[SET];
 #pragma unroll
     for (int j = 0; j < C::CPT; ++j) {
       const int ch = tid + j * kIdxThreads;
@@ -281,14 +307,18 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     if (tid < C::KT) sKs[buf][tid] = pks;
   };
 
-  gload(0);
-  lstore(0);
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  gload(0, Set0{});
+  if (ntiles > 1) gload(1, Set1{});
+  lstore(Set0{});
   __syncthreads();
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
+  auto tile_step = [&](const int tile, auto setc) {
+    constexpr int SET = decltype(setc)::value;
+    constexpr int buf = SET;
     const int kb = c0 + tile * C::KT;
-    if (tile + 1 < ntiles) gload(tile + 1);
+    if (tile + 2 < ntiles) gload(tile + 2, setc);
     // skip waves whose tokens do not see this tile
     if (wmax > kb && wmin < kb + C::KT) {
       // 16-key sub-tiles, software pipelined (128-deep keys): the MFMAs of
@@ -312,11 +342,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
           for (int rt = 0; rt < kRT; ++rt) a[rt] = mfma_f8_16x16x128(qf[rt][s], bf, a[rt]);
         }
       };
-      // epilogue: relu * weight, sum over heads, * k_scale, masked store
-      auto epi = [&](int n, const f32x4* a) {
-        const int kk = n * 16 + col;
-        const float ksc = sKs[buf][kk];
-        const int key = kb + kk;
+      // epilogue: relu * weight, sum over heads, * k_scale (epi_sum), masked
+      // store (epi_store)
+      auto epi_sum = [&](const f32x4* a, float* sum) {
         // 4 independent partial sums per token (short dependency chains)
         float part[C::TPL][4];
 #pragma unroll
@@ -329,14 +357,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
           for (int i = 0; i < 4; ++i)
             part[(4 * rt + i) / (32 / C::TPL)][i] =
                 fmaf(relu(a[rt][i]), weff[rt][i], part[(4 * rt + i) / (32 / C::TPL)][i]);
-        float sum[C::TPL];
 #pragma unroll
         for (int j = 0; j < C::TPL; ++j) sum[j] = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
         if constexpr (C::GPT >= 2) sum[0] = lane_swap_sum<16>(sum[0]);
         if constexpr (C::GPT >= 4) sum[0] = lane_swap_sum<32>(sum[0]);
+      };
+      auto epi_store = [&](int n, const float* sum) {
+        const int kk = n * 16 + col;
+        const float ksc = sKs[buf][kk];
+        const int key = kb + kk;
 #pragma unroll
         for (int j = 0; j < C::TPL; ++j)
           if (store_lane && key >= ls[j] && key < le[j]) orow[j][key] = sum[j] * ksc;
+      };
+      auto epi = [&](int n, const f32x4* a) {
+        float sum[C::TPL];
+        epi_sum(a, sum);
+        epi_store(n, sum);
       };
       // this wave's sub-tiles: all of them, or (key-parallel) every
       // kIdxWaves-th one
@@ -345,8 +382,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
         mm(sub(0), acc[0]);
 #pragma unroll
         for (int j = 0; j < C::NS; ++j) {
-          if (j + 1 < C::NS) mm(sub(j + 1), acc[(j + 1) & 1]);
-          epi(sub(j), acc[j & 1]);
+          float sum[C::TPL];
+          if (j + 1 < C::NS) {
+            mm(sub(j + 1), acc[(j + 1) & 1]);
+            epi_sum(acc[j & 1], sum);
+            // interleave: the B-fragment LDS reads, then each MFMA of
+            // sub-tile j+1 followed by a share of sub-tile j's VALU
+            // epilogue, which the fp8 MFMA (32 cycles) hides
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+            for (int i = 0; i < kRT * C::KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, kIdxVpm, 0);  // VALU
+            }
+          } else {
+            epi_sum(acc[j & 1], sum);
+          }
+          epi_store(sub(j), sum);
         }
       } else {
 #pragma unroll 1
@@ -356,8 +408,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
         }
       }
     }
-    if (tile + 1 < ntiles) lstore(buf ^ 1);
+    if (tile + 1 < ntiles) lstore(std::integral_constant<int, SET ^ 1>{});
     __syncthreads();
+  };
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    tile_step(tile, Set0{});
+    if (tile + 1 < ntiles) tile_step(tile + 1, Set1{});
   }
   };
 
