@@ -235,49 +235,45 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     m[ht] = -1e30f;
     lsum[ht] = 0.f;
   }
-  // indices -> LDS (sanitised: -1 = invalid), sink -> LDS
+  // indices -> LDS (sanitised: -1 = invalid), sink -> LDS.  Per tile, the
+  // first valid index (invalid slots gather that row: finite data whose p is
+  // exactly 0) and whether all 32 are valid: for the first IB*THREADS
+  // indices a half-wave holds one tile in iv[j], so two ballots give both.
   auto sanitise = [&](int v) { return (v >= 0 && v < N) ? v : -1; };
+  static_assert(kBI == 32, "a tile is one half-wave of iv[j]");
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
     const int p = tid + j * C::THREADS;
-    if (p < nidx) sIdx[p] = sanitise(iv[j]);
+    const int v = sanitise(iv[j]);
+    if (p < nidx) sIdx[p] = v;
+    const uint64_t mk = __ballot(v >= 0);
+    const uint32_t mh = (uint32_t)(mk >> (lane & 32));
+    const int fl = mh ? __builtin_ctz(mh) : 0;
+    const int first = __shfl(v, (lane & 32) + fl, kWave);
+    const int t = p / kBI;
+    if ((lane & 31) == 0 && t < ntiles) {
+      sFirst[t] = mh ? first : -1;
+      sFull[t] = mh == 0xffffffffu;
+    }
   }
   for (int p = tid + IB * C::THREADS; p < nidx; p += C::THREADS)
     sIdx[p] = sanitise(p < klen ? ridx[p] : -1);
   if (tid < Hq) sSink[tid] = skv;
   __syncthreads();
-  // list of tiles holding a valid index; first valid index of each tile
-  // (invalid slots gather that row: finite data whose p is exactly 0)
-  if (wave == 0) {
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int base = 0;
-    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
-      const int t = t0 + lane;
-      int first = -1;
-      if (t < ntiles) {
-        bool full = true;
-        for (int r = kBI - 1; r >= 0; --r) {
-          const int v = sIdx[t * kBI + r];
-          first = v >= 0 ? v : first;
-          full = full && v >= 0;
-        }
-        sFirst[t] = first;
-        sFull[t] = full;
-      }
-      const bool f = first >= 0;
-      const uint64_t mk = __ballot(f);
-      if (f) sList[base + __popcll(mk & lt)] = t;
-      base += __popcll(mk);
+  // tiles beyond the first IB*THREADS indices: one lane per tile scans it
+  constexpr int T0 = IB * C::THREADS / kBI;
+  for (int t = T0 + tid; t < ntiles; t += C::THREADS) {
+    int first = -1;
+    bool full = true;
+    for (int r = kBI - 1; r >= 0; --r) {
+      const int v = sIdx[t * kBI + r];
+      first = v >= 0 ? v : first;
+      full = full && v >= 0;
     }
-    if (lane == 0) sNvt = base;
+    sFirst[t] = first;
+    sFull[t] = full;
   }
-#pragma unroll
-  for (int c = C::QR; c < C::QC; ++c)
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) sQ[c - C::QR][wave][ht][lane] = ql[c - C::QR][ht];
-  __syncthreads();
-  const int nvt = sNvt;
-
+  if (ntiles > T0) __syncthreads();  // uniform
   // ---- tile staging: VGPRs, then LDS ----------------------------------------
   // Each thread moves NC chunks of a tile (chunk = 8 elements of one row: 16
   // bytes of bf16 or 8 fp8 codes).  The loads of tile it+1 are issued one by
@@ -356,6 +352,50 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     for (int k = 0; k < NC; ++k) store_chunk(dst, k);
     store_scale(dsc);
   };
+  // Tile 0 -- the first tile of nearly every row -- is gathered while the
+  // tile list is built; invalid slots load nothing (zeros: finite, masked,
+  // p exactly 0).  Used by the first pass if tile 0 holds a valid index.
+  {
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) {
+      const int r = p * C::RPP + srow;
+      grow[p] = (kBI % C::RPP == 0 || r < kBI) && r < nidx ? sIdx[r] : -1;
+    }
+    if constexpr (FP8) {
+      if (tid < kBI) {
+        const int row = tid < nidx ? sIdx[tid] : -1;
+        pscale = row >= 0 ? kv_scale[(size_t)b * N + row] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      chunk_t v{};
+      if (chunk_ok(k) && grow[k / C::CPT] >= 0)
+        v = *reinterpret_cast<const chunk_t*>(kvb + (size_t)grow[k / C::CPT] * DQK +
+                                              C::TPR * (k % C::CPT) * 8);
+      pre[k] = v;
+    }
+  }
+  // list of tiles holding a valid index, ascending
+  if (wave == 0) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+      const int t = t0 + lane;
+      const bool f = t < ntiles && sFirst[t] >= 0;
+      const uint64_t mk = __ballot(f);
+      if (f) sList[base + __popcll(mk & lt)] = t;
+      base += __popcll(mk);
+    }
+    if (lane == 0) sNvt = base;
+  }
+#pragma unroll
+  for (int c = C::QR; c < C::QC; ++c)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) sQ[c - C::QR][wave][ht][lane] = ql[c - C::QR][ht];
+  __syncthreads();
+  const int nvt = sNvt;
+
   // Staging schedule (at most half the chunks in registers at a time): the
   // first GH chunks are loaded over the first half of the QK^T k-steps and
   // written to LDS over the second half (the other buffer is free since the
@@ -365,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   constexpr int GH = (NC + 1) / 2, QH = C::QC / 2;
   // QK^T k-step after which chunk k is loaded
   auto gstep = [](int k) {
-    return k < GH ? (k * QH) / GH : QH + ((k - GH) * (C::QC - QH)) / (NC - GH);
+    return k < GH ? (k * QH) / GH : QH + ((k - GH) * (C::QC - QH)) / (NC - GH > 0 ? NC - GH : 1);
   };
   // QK^T k-step after which chunk k is stored (chunks k < GH; QC: after the
   // last k-step, beside the softmax, whose VALU work leaves LDS idle), PV
@@ -553,7 +593,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   for (int mode = 0;;) {
     if (tid == 0) sFlag[0] = 0;
     if (nvt > 0) {
-      gload(sList[0]);
+      if (mode != 0 || sList[0] != 0) gload(sList[0]);  // else: tile 0, gathered above
       lstore(sKV[0], sSc[0]);
     }
 #pragma unroll 1
