@@ -251,76 +251,61 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Writes to o[0..K) the positions (first + i, or cand[i] when GATHER) of the
-// K largest of len > K keys src[i] (or src[cand[i]]), i < len, in ascending
-// order of i.  Keys at most 256*KR.  Workgroup of kRowThreads; the LDS
-// arrays are the caller's.
+// One MSD round's threshold: hist[0..nb) counts the remaining keys by digit
+// (larger digit = larger key); returns the digit bin holding the krem-th
+// largest of them and the number of keys in the bins above it.  Called by
+// every thread of a kRowThreads workgroup; hist may be in LDS or in global
+// memory.
+__device__ __forceinline__ int2 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
+                                              int* sSel) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bpt = nb / kRowThreads;  // bins per thread
+  int tsum = 0;
+  for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
+  const int incl_w = wave_incl_scan(tsum);
+  if (lane == 63) sRed[wave] = incl_w;
+  __syncthreads();
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    const int t = sRed[w];
+    pre += w < wave ? t : 0;
+    total += t;
+  }
+  int above = total - (pre + incl_w);  // keys in bins of higher threads
+  if (above < krem && krem <= above + tsum) {  // exactly one thread
+    for (int j = bpt - 1; j >= 0; --j) {
+      const int c = (int)hist[tid * bpt + j];
+      if (above < krem && krem <= above + c) {
+        sSel[0] = tid * bpt + j;
+        sSel[1] = above;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+  return make_int2(sSel[0], sSel[1]);
+}
+
+// Digit layout of the 32-bit key: rounds of 11, 11 and 10 bits.
+__host__ __device__ constexpr int digit_bits(int round) { return round < 2 ? 11 : 10; }
+__host__ __device__ constexpr int digit_shift(int round) {
+  return round == 0 ? 21 : (round == 1 ? 10 : 0);
+}
+
+// Emission of a workgroup's keys (wave w holds positions w*64*KR + c*64 +
+// lane, len of them): every key > tau and the first n_eq keys == tau of the
+// whole row go to o in ascending position order.  gt0 / eq0: keys > tau /
+// == tau at positions before this workgroup's (other workgroups of the same
+// row).  Writes o[pos] = first + i, or cand[i] when GATHER.
 template <int KR, bool GATHER>
-__device__ __forceinline__ void row_select(const float* __restrict__ src,
-                                           const int* __restrict__ cand, int len, int first,
-                                           int K, int* __restrict__ o, uint32_t* hist, int* sRed,
-                                           int* sSel, int (*sCnt)[kRowWaves]) {
+__device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int len, uint32_t tau,
+                                              int n_eq, int gt0, int eq0, int first,
+                                              const int* __restrict__ cand, int K,
+                                              int* __restrict__ o, int (*sCnt)[kRowWaves]) {
   constexpr int SEG = kWave * KR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = wave * SEG;
-  uint32_t keys[KR];
-#pragma unroll
-  for (int c = 0; c < KR; ++c) {
-    const int i = base + c * kWave + lane;
-    keys[c] = i < len ? order_key(GATHER ? src[cand[i]] : src[i]) : 0u;
-  }
-
-  uint32_t prefix = 0;
-  int krem = K, above_total = 0;
-#pragma unroll
-  for (int round = 0; round < 3; ++round) {
-    const int bits = round < 2 ? 11 : 10;
-    const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
-    const int nb = 1 << bits;
-    const int bpt = nb / kRowThreads;  // bins per thread
-    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < KR; ++c) {
-      if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
-      const int i = base + c * kWave + lane;
-      const uint32_t u = keys[c];
-      if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
-        atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    int tsum = 0;
-    for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
-    const int incl_w = wave_incl_scan(tsum);
-    if (lane == 63) sRed[wave] = incl_w;
-    __syncthreads();
-    int pre = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      const int t = sRed[w];
-      pre += w < wave ? t : 0;
-      total += t;
-    }
-    int above = total - (pre + incl_w);  // keys in bins of higher threads
-    if (above < krem && krem <= above + tsum) {  // exactly one thread
-      for (int j = bpt - 1; j >= 0; --j) {
-        const int c = (int)hist[tid * bpt + j];
-        if (above < krem && krem <= above + c) {
-          sSel[0] = tid * bpt + j;
-          sSel[1] = above;
-        }
-        above += c;
-      }
-    }
-    __syncthreads();
-    const int bin = sSel[0], ab = sSel[1];
-    prefix = (prefix << bits) | (uint32_t)bin;
-    krem -= ab;
-    above_total += ab;
-  }
-  const uint32_t tau = prefix;
-  const int n_eq = K - above_total;
-
   int gtc = 0, eqc = 0;
 #pragma unroll
   for (int c = 0; c < KR; ++c) {
@@ -334,7 +319,7 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
     sCnt[1][wave] = eqc;
   }
   __syncthreads();
-  int gt_base = 0, eq_base = 0;
+  int gt_base = gt0, eq_base = eq0;
 #pragma unroll
   for (int w = 0; w < kRowWaves; ++w) {
     gt_base += w < wave ? sCnt[0][w] : 0;
@@ -359,6 +344,50 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
     sel_run += __popcll(mgt) + min((int)__popcll(meq), eq_left);
     eq_run += __popcll(meq);
   }
+}
+
+// Writes to o[0..K) the positions (first + i, or cand[i] when GATHER) of the
+// K largest of len > K keys src[i] (or src[cand[i]]), i < len, in ascending
+// order of i.  Keys at most 256*KR.  Workgroup of kRowThreads; the LDS
+// arrays are the caller's.
+template <int KR, bool GATHER>
+__device__ __forceinline__ void row_select(const float* __restrict__ src,
+                                           const int* __restrict__ cand, int len, int first,
+                                           int K, int* __restrict__ o, uint32_t* hist, int* sRed,
+                                           int* sSel, int (*sCnt)[kRowWaves]) {
+  constexpr int SEG = kWave * KR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = wave * SEG;
+  uint32_t keys[KR];
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    const int i = base + c * kWave + lane;
+    keys[c] = i < len ? order_key(GATHER ? src[cand[i]] : src[i]) : 0u;
+  }
+
+  uint32_t prefix = 0;
+  int krem = K, above_total = 0;
+#pragma unroll
+  for (int round = 0; round < 3; ++round) {
+    const int bits = digit_bits(round), shift = digit_shift(round);
+    const int nb = 1 << bits;
+    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < KR; ++c) {
+      if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
+      const int i = base + c * kWave + lane;
+      const uint32_t u = keys[c];
+      if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
+        atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    const int2 sel = threshold_bin(hist, nb, krem, sRed, sSel);
+    prefix = (prefix << bits) | (uint32_t)sel.x;
+    krem -= sel.y;
+    above_total += sel.y;
+  }
+  emit_selected<KR, GATHER>(keys, len, prefix, K - above_total, 0, 0, first, cand, K, o, sCnt);
 }
 
 #define DSA_TOPK_LDS                                  \
@@ -453,6 +482,172 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __
   row_select<KR, true>(logits + r * (size_t)N, c, n, 0, K, o, hist, sRed, sSel, sCnt);
 }
 
+// ---- few long rows: several workgroups per row -----------------------------
+// With few rows (decode) one workgroup per row leaves most CUs idle.  Each
+// row is cut into segments of kSplitKeys keys, one workgroup each, and the
+// three digit rounds run as separate launches: every workgroup adds its
+// segment's LDS histogram of the round's digit (keys matching the prefix of
+// the earlier rounds) into the row's global histogram, and the next launch's
+// workgroups each derive the thresholds from the row's completed histograms.
+// Then every segment counts its keys > tau and == tau, and each segment
+// emits its selected keys at the offset given by the counts of the segments
+// before it: ascending order, ties to the lower index, no atomics on the
+// output.  Per row the workspace holds 3 x 2048 histogram words and two
+// counts per segment.
+constexpr int kSplitKR = 16;
+constexpr int kSplitKeys = kRowThreads * kSplitKR;
+constexpr int kSplitHist = 3 * 2048;  // histogram words per row
+
+__global__ __launch_bounds__(kRowThreads) void topk_split_zero_kernel(uint32_t* __restrict__ hist) {
+  uint32_t* h = hist + blockIdx.x * (size_t)kSplitHist;
+  for (int i = threadIdx.x; i < kSplitHist; i += kRowThreads) h[i] = 0u;
+}
+
+// Segment of workgroup blockIdx.x (row r, segment seg): the keys in VGPRs in
+// the wave-contiguous layout of emit_selected.  Returns the number of keys
+// of the segment (<= 0: none), or -1 when the row has at most K keys.
+__device__ __forceinline__ int split_load(const float* __restrict__ logits,
+                                          const int* __restrict__ ks, const int* __restrict__ ke,
+                                          int N, int K, int nseg, size_t& r, int& s0,
+                                          uint32_t (&keys)[kSplitKR]) {
+  r = blockIdx.x / nseg;
+  const int seg = (int)(blockIdx.x % nseg);
+  const int s = clampi(ks[r], 0, N);
+  const int e = clampi(ke[r], s, N);
+  if (e - s <= K) return -1;
+  s0 = s + seg * kSplitKeys;
+  const int n = min(e - s0, kSplitKeys);
+  if (n <= 0) return 0;
+  const float* src = logits + r * (size_t)N + s0;
+  const int base = (threadIdx.x >> 6) * (kWave * kSplitKR) + (threadIdx.x & 63);
+#pragma unroll
+  for (int c = 0; c < kSplitKR; ++c) {
+    const int i = base + c * kWave;
+    keys[c] = i < n ? order_key(src[i]) : 0u;
+  }
+  return n;
+}
+
+// Thresholds of rounds 0..nr-1 from the row's histograms h: the key prefix
+// they fix, and the number of keys above it.
+__device__ __forceinline__ void split_prefix(const uint32_t* h, int nr, int K, uint32_t& prefix,
+                                             int& above, int* sRed, int* sSel) {
+  prefix = 0;
+  above = 0;
+  for (int q = 0; q < nr; ++q) {
+    const int2 sel = threshold_bin(h + q * 2048, 1 << digit_bits(q), K - above, sRed, sSel);
+    prefix = (prefix << digit_bits(q)) | (uint32_t)sel.x;
+    above += sel.y;
+  }
+}
+
+// Round ROUND: the segment's digit histogram of the keys matching the prefix
+// of the earlier rounds, added into the row's histogram ROUND.
+template <int ROUND>
+__global__ __launch_bounds__(kRowThreads) void topk_split_hist_kernel(
+    const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
+    uint32_t* __restrict__ hist, int N, int K, int nseg) {
+  __shared__ uint32_t lh[2048];
+  __shared__ int sRed[kRowWaves];
+  __shared__ int sSel[2];
+  constexpr int bits = digit_bits(ROUND), shift = digit_shift(ROUND), nb = 1 << bits;
+  size_t r;
+  int s0;
+  uint32_t keys[kSplitKR];
+  const int n = split_load(logits, ks, ke, N, K, nseg, r, s0, keys);
+  if (n <= 0) return;  // workgroup-uniform
+  uint32_t* h = hist + r * kSplitHist;
+  uint32_t prefix;
+  int above;
+  split_prefix(h, ROUND, K, prefix, above, sRed, sSel);
+  for (int i = threadIdx.x; i < nb; i += kRowThreads) lh[i] = 0u;
+  __syncthreads();
+  const int base = (threadIdx.x >> 6) * (kWave * kSplitKR) + (threadIdx.x & 63);
+#pragma unroll
+  for (int c = 0; c < kSplitKR; ++c) {
+    if ((threadIdx.x >> 6) * (kWave * kSplitKR) + c * kWave >= n) break;  // wave-uniform
+    const uint32_t u = keys[c];
+    if (base + c * kWave < n && (ROUND == 0 || (u >> (shift + bits)) == prefix))
+      atomicAdd(&lh[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += kRowThreads) {
+    const uint32_t v = lh[i];
+    if (v) atomicAdd(&h[ROUND * 2048 + i], v);
+  }
+}
+
+// The row's exact threshold key tau; the segment's keys > tau and == tau.
+__global__ __launch_bounds__(kRowThreads) void topk_split_count_kernel(
+    const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
+    const uint32_t* __restrict__ hist, int* __restrict__ cnt, int N, int K, int nseg) {
+  __shared__ int sRed[kRowWaves];
+  __shared__ int sSel[2];
+  __shared__ int sCnt[2][kRowWaves];
+  size_t r;
+  int s0;
+  uint32_t keys[kSplitKR];
+  const int n = split_load(logits, ks, ke, N, K, nseg, r, s0, keys);
+  if (n <= 0) return;
+  uint32_t tau;
+  int above;
+  split_prefix(hist + r * kSplitHist, 3, K, tau, above, sRed, sSel);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = wave * (kWave * kSplitKR) + lane;
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int c = 0; c < kSplitKR; ++c) {
+    const bool v = base + c * kWave < n;
+    gtc += (int)__popcll(__ballot(v && keys[c] > tau));
+    eqc += (int)__popcll(__ballot(v && keys[c] == tau));
+  }
+  if (lane == 0) {
+    sCnt[0][wave] = gtc;
+    sCnt[1][wave] = eqc;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) t += sCnt[threadIdx.x][w];
+    cnt[blockIdx.x * (size_t)2 + threadIdx.x] = t;
+  }
+}
+
+// Emission (and the whole output of rows of at most K keys, by segment 0).
+__global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
+    const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
+    const uint32_t* __restrict__ hist, const int* __restrict__ cnt, int* __restrict__ out, int N,
+    int K, int nseg) {
+  __shared__ int sRed[kRowWaves];
+  __shared__ int sSel[2];
+  __shared__ int sCnt[2][kRowWaves];
+  size_t r;
+  int s0;
+  uint32_t keys[kSplitKR];
+  const int n = split_load(logits, ks, ke, N, K, nseg, r, s0, keys);
+  const int seg = (int)(blockIdx.x % nseg);
+  int* o = out + r * (size_t)K;
+  if (n < 0) {  // at most K keys: the window, then -1 padding
+    if (seg == 0) {
+      const int s = clampi(ks[r], 0, N);
+      const int len = clampi(ke[r], s, N) - s;
+      for (int i = threadIdx.x; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
+    }
+    return;
+  }
+  if (n == 0) return;
+  uint32_t tau;
+  int above;
+  split_prefix(hist + r * kSplitHist, 3, K, tau, above, sRed, sSel);
+  const int* rc = cnt + (r * nseg) * (size_t)2;
+  int gt0 = 0, eq0 = 0;
+  for (int q = 0; q < seg; ++q) {
+    gt0 += rc[2 * q];
+    eq0 += rc[2 * q + 1];
+  }
+  emit_selected<kSplitKR, false>(keys, n, tau, K - above, gt0, eq0, s0, nullptr, K, o, sCnt);
+}
 
 }  // namespace
 
@@ -468,13 +663,45 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
                        a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
     return hipGetLastError();
   }
+  // Few rows (decode) with windows that may pass 8192 keys: several
+  // workgroups per row, every row (see the split kernels).
+  const long long split_nseg = (a.N + kSplitKeys - 1) / kSplitKeys;
+  if (rows < 256 && a.N > kRowThreads * (8192 / kRowThreads) &&
+      rows * split_nseg * kRowThreads <= 0xffffffffLL) {
+    const int nseg = (int)split_nseg;
+    const size_t hist_bytes = (size_t)rows * kSplitHist * sizeof(uint32_t);
+    const size_t ws_bytes = hist_bytes + (size_t)rows * nseg * 2 * sizeof(int);
+    keep_pool_memory();
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, ws_bytes, stream) == hipSuccess) {
+      uint32_t* hist = static_cast<uint32_t*>(ws);
+      int* cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + hist_bytes);
+      const dim3 grid((unsigned)(rows * nseg)), block(kRowThreads);
+      hipLaunchKernelGGL(topk_split_zero_kernel, dim3((unsigned)rows), block, 0, stream, hist);
+      hipLaunchKernelGGL(topk_split_hist_kernel<0>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         hist, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_hist_kernel<1>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         hist, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_hist_kernel<2>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         hist, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_count_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         hist, cnt, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_emit_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         hist, cnt, a.topk_idxs, (int)a.N, (int)a.K, nseg);
+      const hipError_t lerr = hipGetLastError();
+      const hipError_t ferr = hipFreeAsync(ws, stream);
+      return lerr != hipSuccess ? lerr : ferr;
+    }
+    (void)hipGetLastError();
+  }
   const int nseg = (int)((a.N + kSegKeys - 1) / kSegKeys);
   const long long ncand = (long long)nseg * a.K;
   const size_t ws_bytes = (size_t)rows * ncand * sizeof(int);
   const bool two_level = a.N > kSegKeys && a.K <= kSegKeys && ncand <= kRowThreads * 64 &&
                          rows * nseg <= 0x7fffffffLL && ws_bytes <= ((size_t)256 << 20);
-  // With few rows (decode) and two levels, the two-level kernels take every
-  // row, as one more launch would cost more than the short rows gain.
+  // With few rows and two levels (the split kernels could not get their
+  // workspace), the two-level kernels take every row, as one more launch
+  // would cost more than the short rows gain.
   const bool rows_first = !(two_level && rows < 256);
   const int skip_len = rows_first ? kRowThreads * (8192 / kRowThreads) : 0;
   hipError_t err = hipSuccess;

@@ -112,17 +112,34 @@ def test_topk_workloads(name, nrows):
 
 @pytest.mark.parametrize("kind", ["special", "ties", "narrow"])
 @pytest.mark.parametrize("K", [100, 2048, 4096])
-def test_topk_two_level_rows(kind, K):
-    """N in (8192, 65536]: long rows are cut into 8192-key segments whose
-    top-K candidates are then reduced; lengths straddle segment boundaries."""
+def test_topk_split_rows(kind, K):
+    """Few rows with N > 8192: every row is cut into 4096-key segments, one
+    workgroup each, that share the row's digit histograms; lengths straddle
+    segment boundaries."""
     rng = np.random.default_rng(K + len(kind))
     B, M, N = 1, 10, 40000
     lg = _dist(kind, (B, M, N), rng)
     # ... plus an empty row and a row shorter than K (written as -1 padded)
     ks = np.array([[0, 0, 0, 0, 0, 100, 31000, 5, 7, 0]], np.int32)
     ke = np.array([[N, K + 1, 8192, 8193, 16384 + 7, 24000, N, 5 + K, 7, K - 1]], np.int32)
-    log(f"topk two-level {kind} K={K}")
-    _compare(lg, ks, ke, K, what=f"two-level {kind}/K{K}")
+    log(f"topk split rows {kind} K={K}")
+    _compare(lg, ks, ke, K, what=f"split rows {kind}/K{K}")
+
+
+@pytest.mark.parametrize("K", [100, 2048])
+def test_topk_two_level_many_rows(K):
+    """At least 256 rows with N > 8192: rows of up to 8192 keys go to the
+    register-resident kernel; longer ones are cut into 8192-key segments
+    whose top-K candidates are then reduced."""
+    rng = np.random.default_rng(31 + K)
+    B, M, N = 1, 300, 20000
+    lg = _dist("ties" if K == 100 else "special", (B, M, N), rng)
+    ks = rng.integers(0, 3000, (B, M)).astype(np.int32)
+    ke = (ks + rng.integers(0, N - 3000, (B, M))).astype(np.int32)
+    ks[0, :6] = [0, 0, 0, 5, 0, 19000]
+    ke[0, :6] = [N, 8192, 8193, 16390, K, N]
+    log(f"topk two-level many rows K={K}")
+    _compare(lg, ks, ke, K, what=f"two-level many rows K{K}")
 
 
 def test_topk_many_long_rows_streaming():
