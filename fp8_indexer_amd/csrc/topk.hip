@@ -487,20 +487,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(const float* __
 // row is cut into segments of kSplitKeys keys, one workgroup each, and the
 // three digit rounds run as separate launches: every workgroup adds its
 // segment's LDS histogram of the round's digit (keys matching the prefix of
-// the earlier rounds) into the row's global histogram, and the next launch's
-// workgroups each derive the thresholds from the row's completed histograms.
-// Then every segment counts its keys > tau and == tau, and each segment
-// emits its selected keys at the offset given by the counts of the segments
-// before it: ascending order, ties to the lower index, no atomics on the
-// output.  Per row the workspace holds 3 x 2048 histogram words and two
-// counts per segment.
+// the earlier rounds) into the row's global histogram, and each workgroup of
+// a later launch derives the earlier rounds' threshold digits from the
+// row's completed histograms (the launch boundary orders them; a fence per
+// workgroup would write back the XCD's whole L2).  The last round also
+// keeps, per segment, its keys above the 22-bit prefix and the suffix sums
+// of its own last-digit histogram, from which the emission launch reads
+// each earlier segment's keys > tau and == tau with two loads: every segment
+// writes its selected keys at the offset they give, in ascending order with
+// ties to the lower index, and no atomics touch the output.
 constexpr int kSplitKR = 16;
 constexpr int kSplitKeys = kRowThreads * kSplitKR;
-constexpr int kSplitHist = 3 * 2048;  // histogram words per row
+// per row: 3 x 2048 histogram words; per segment: 1024 suffix sums and the
+// count above the 22-bit prefix (kSplitSegWords, padded)
+constexpr int kSplitRowWords = 3 * 2048;
+constexpr int kSplitSegWords = 1028;
 
-__global__ __launch_bounds__(kRowThreads) void topk_split_zero_kernel(uint32_t* __restrict__ hist) {
-  uint32_t* h = hist + blockIdx.x * (size_t)kSplitHist;
-  for (int i = threadIdx.x; i < kSplitHist; i += kRowThreads) h[i] = 0u;
+__global__ __launch_bounds__(kRowThreads) void topk_split_zero_kernel(uint32_t* __restrict__ ws) {
+  uint32_t* h = ws + blockIdx.x * (size_t)kSplitRowWords;
+  for (int i = threadIdx.x; i < kSplitRowWords; i += kRowThreads) h[i] = 0u;
 }
 
 // Segment of workgroup blockIdx.x (row r, segment seg): the keys in VGPRs in
@@ -529,7 +534,7 @@ __device__ __forceinline__ int split_load(const float* __restrict__ logits,
 }
 
 // Thresholds of rounds 0..nr-1 from the row's histograms h: the key prefix
-// they fix, and the number of keys above it.
+// they fix and the number of keys above it.
 __device__ __forceinline__ void split_prefix(const uint32_t* h, int nr, int K, uint32_t& prefix,
                                              int& above, int* sRed, int* sSel) {
   prefix = 0;
@@ -541,84 +546,83 @@ __device__ __forceinline__ void split_prefix(const uint32_t* h, int nr, int K, u
   }
 }
 
-// Round ROUND: the segment's digit histogram of the keys matching the prefix
-// of the earlier rounds, added into the row's histogram ROUND.
+// Round ROUND: the segment's histogram of the digit over the keys that match
+// the prefix fixed by the earlier rounds, added into the row's histogram.
 template <int ROUND>
-__global__ __launch_bounds__(kRowThreads) void topk_split_hist_kernel(
+__global__ __launch_bounds__(kRowThreads) void topk_split_round_kernel(
     const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
-    uint32_t* __restrict__ hist, int N, int K, int nseg) {
+    uint32_t* __restrict__ ws, int N, int K, int nseg) {
   __shared__ uint32_t lh[2048];
   __shared__ int sRed[kRowWaves];
   __shared__ int sSel[2];
   constexpr int bits = digit_bits(ROUND), shift = digit_shift(ROUND), nb = 1 << bits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   size_t r;
   int s0;
   uint32_t keys[kSplitKR];
   const int n = split_load(logits, ks, ke, N, K, nseg, r, s0, keys);
   if (n <= 0) return;  // workgroup-uniform
-  uint32_t* h = hist + r * kSplitHist;
+  uint32_t* row = ws + r * kSplitRowWords;
+  uint32_t* h = row + ROUND * 2048;
   uint32_t prefix;
   int above;
-  split_prefix(h, ROUND, K, prefix, above, sRed, sSel);
-  for (int i = threadIdx.x; i < nb; i += kRowThreads) lh[i] = 0u;
+  split_prefix(row, ROUND, K, prefix, above, sRed, sSel);
+  for (int i = tid; i < nb; i += kRowThreads) lh[i] = 0u;
   __syncthreads();
-  const int base = (threadIdx.x >> 6) * (kWave * kSplitKR) + (threadIdx.x & 63);
-#pragma unroll
-  for (int c = 0; c < kSplitKR; ++c) {
-    if ((threadIdx.x >> 6) * (kWave * kSplitKR) + c * kWave >= n) break;  // wave-uniform
-    const uint32_t u = keys[c];
-    if (base + c * kWave < n && (ROUND == 0 || (u >> (shift + bits)) == prefix))
-      atomicAdd(&lh[(u >> shift) & (uint32_t)(nb - 1)], 1u);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < nb; i += kRowThreads) {
-    const uint32_t v = lh[i];
-    if (v) atomicAdd(&h[ROUND * 2048 + i], v);
-  }
-}
-
-// The row's exact threshold key tau; the segment's keys > tau and == tau.
-__global__ __launch_bounds__(kRowThreads) void topk_split_count_kernel(
-    const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
-    const uint32_t* __restrict__ hist, int* __restrict__ cnt, int N, int K, int nseg) {
-  __shared__ int sRed[kRowWaves];
-  __shared__ int sSel[2];
-  __shared__ int sCnt[2][kRowWaves];
-  size_t r;
-  int s0;
-  uint32_t keys[kSplitKR];
-  const int n = split_load(logits, ks, ke, N, K, nseg, r, s0, keys);
-  if (n <= 0) return;
-  uint32_t tau;
-  int above;
-  split_prefix(hist + r * kSplitHist, 3, K, tau, above, sRed, sSel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int base = wave * (kWave * kSplitKR) + lane;
-  int gtc = 0, eqc = 0;
+  int gt = 0;  // keys above the prefix (last round)
 #pragma unroll
   for (int c = 0; c < kSplitKR; ++c) {
+    if (wave * (kWave * kSplitKR) + c * kWave >= n) break;  // wave-uniform
+    const uint32_t u = keys[c];
     const bool v = base + c * kWave < n;
-    gtc += (int)__popcll(__ballot(v && keys[c] > tau));
-    eqc += (int)__popcll(__ballot(v && keys[c] == tau));
-  }
-  if (lane == 0) {
-    sCnt[0][wave] = gtc;
-    sCnt[1][wave] = eqc;
+    if (v && (ROUND == 0 || (u >> (shift + bits)) == prefix))
+      atomicAdd(&lh[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+    if (ROUND == 2) gt += (int)__popcll(__ballot(v && (u >> (shift + bits)) > prefix));
   }
   __syncthreads();
-  if (threadIdx.x < 2) {
-    int t = 0;
+  int tsum = 0;
+  constexpr int bpt = nb / kRowThreads;
+  uint32_t hv[bpt];
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) t += sCnt[threadIdx.x][w];
-    cnt[blockIdx.x * (size_t)2 + threadIdx.x] = t;
+  for (int j = 0; j < bpt; ++j) {
+    hv[j] = lh[tid * bpt + j];
+    tsum += (int)hv[j];
+    if (hv[j]) atomicAdd(&h[tid * bpt + j], hv[j]);
+  }
+  if constexpr (ROUND == 2) {
+    // this segment's suffix sums of the last-digit histogram, and its keys
+    // above the 22-bit prefix
+    const int incl_w = wave_incl_scan(tsum);
+    if (lane == 63) sRed[wave] = incl_w;
+    __syncthreads();
+    int pre = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const int x = sRed[w];
+      pre += w < wave ? x : 0;
+      total += x;
+    }
+    uint32_t* sg = ws + (size_t)gridDim.x / nseg * kSplitRowWords +
+                   (size_t)blockIdx.x * kSplitSegWords;
+    int suf = total - (pre + incl_w - tsum);
+#pragma unroll
+    for (int j = 0; j < bpt; ++j) {
+      sg[tid * bpt + j] = (uint32_t)suf;
+      suf -= (int)hv[j];
+    }
+    if (lane == 0) sSel[0] = 0;
+    __syncthreads();
+    if (lane == 0) atomicAdd(&sSel[0], gt);
+    __syncthreads();
+    if (tid == 0) sg[1024] = (uint32_t)sSel[0];
   }
 }
 
 // Emission (and the whole output of rows of at most K keys, by segment 0).
 __global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
     const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
-    const uint32_t* __restrict__ hist, const int* __restrict__ cnt, int* __restrict__ out, int N,
-    int K, int nseg) {
+    const uint32_t* __restrict__ ws, int* __restrict__ out, int N, int K, int nseg) {
   __shared__ int sRed[kRowWaves];
   __shared__ int sSel[2];
   __shared__ int sCnt[2][kRowWaves];
@@ -639,12 +643,16 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
   if (n == 0) return;
   uint32_t tau;
   int above;
-  split_prefix(hist + r * kSplitHist, 3, K, tau, above, sRed, sSel);
-  const int* rc = cnt + (r * nseg) * (size_t)2;
+  split_prefix(ws + r * kSplitRowWords, 3, K, tau, above, sRed, sSel);
+  const int d = (int)(tau & 1023u);
+  const uint32_t* sg = ws + (size_t)gridDim.x / nseg * kSplitRowWords +
+                       (size_t)(r * nseg) * kSplitSegWords;
   int gt0 = 0, eq0 = 0;
   for (int q = 0; q < seg; ++q) {
-    gt0 += rc[2 * q];
-    eq0 += rc[2 * q + 1];
+    const uint32_t* x = sg + (size_t)q * kSplitSegWords;
+    const int a1 = d < 1023 ? (int)x[d + 1] : 0;
+    gt0 += (int)x[1024] + a1;
+    eq0 += (int)x[d] - a1;
   }
   emit_selected<kSplitKR, false>(keys, n, tau, K - above, gt0, eq0, s0, nullptr, K, o, sCnt);
 }
@@ -669,25 +677,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (rows < 256 && a.N > kRowThreads * (8192 / kRowThreads) &&
       rows * split_nseg * kRowThreads <= 0xffffffffLL) {
     const int nseg = (int)split_nseg;
-    const size_t hist_bytes = (size_t)rows * kSplitHist * sizeof(uint32_t);
-    const size_t ws_bytes = hist_bytes + (size_t)rows * nseg * 2 * sizeof(int);
+    const size_t ws_bytes =
+        ((size_t)rows * kSplitRowWords + (size_t)rows * nseg * kSplitSegWords) * sizeof(uint32_t);
     keep_pool_memory();
     void* ws = nullptr;
     if (hipMallocAsync(&ws, ws_bytes, stream) == hipSuccess) {
-      uint32_t* hist = static_cast<uint32_t*>(ws);
-      int* cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + hist_bytes);
+      uint32_t* w = static_cast<uint32_t*>(ws);
       const dim3 grid((unsigned)(rows * nseg)), block(kRowThreads);
-      hipLaunchKernelGGL(topk_split_zero_kernel, dim3((unsigned)rows), block, 0, stream, hist);
-      hipLaunchKernelGGL(topk_split_hist_kernel<0>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         hist, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_hist_kernel<1>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         hist, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_hist_kernel<2>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         hist, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_count_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         hist, cnt, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_emit_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         hist, cnt, a.topk_idxs, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_zero_kernel, dim3((unsigned)rows), block, 0, stream, w);
+      hipLaunchKernelGGL(topk_split_round_kernel<0>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         w, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_round_kernel<1>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         w, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_round_kernel<2>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                         w, (int)a.N, (int)a.K, nseg);
+      hipLaunchKernelGGL(topk_split_emit_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke, w,
+                         a.topk_idxs, (int)a.N, (int)a.K, nseg);
       const hipError_t lerr = hipGetLastError();
       const hipError_t ferr = hipFreeAsync(ws, stream);
       return lerr != hipSuccess ? lerr : ferr;
