@@ -52,11 +52,16 @@ constexpr int kIdxVpm = DSA_IDX_VPM;
 // KP (key-parallel, for decode-like inputs with at most TW tokens per batch
 // entry): all waves of a workgroup hold the same tokens and each takes one
 // 16-key sub-tile of every key tile, instead of each wave owning its tokens.
-template <int H, int D, bool KP>
+// RT: 16-row MFMA tiles per wave (kRT; H / 16 for one token per wave, so
+// that a single decode token fills every MFMA row).
+template <int H, int D, bool KP, int RT_ = kRT>
 struct IdxCfg {
   static_assert(H == 4 || H == 8 || H == 16 || H == 32 || H == 64 || H == 128, "H");
   static_assert(D == 64 || D == 128 || D == 256, "D");
-  static constexpr int TW = kRowsPerWave / H;  // tokens per wave
+  static_assert(RT_ == kRT || (KP && RT_ * 16 == H), "row tiles");
+  static constexpr int RT = RT_;
+  static constexpr int GR = 4 * RT;            // rows per lane group
+  static constexpr int TW = 16 * RT / H;       // tokens per wave
   static constexpr int TB = KP ? TW : TW * kIdxWaves;  // tokens per workgroup
   static constexpr int KS = (D + 127) / 128;   // 128-deep MFMA steps
   static constexpr int CPR = D / 16;           // 16-byte chunks per key row
@@ -68,12 +73,12 @@ struct IdxCfg {
   static constexpr int CHUNKS = KT * CPR;
   static constexpr int CPT = (CHUNKS + kIdxThreads - 1) / kIdxThreads;
   // Row placement: C element (row tile rt, lane group g, i) holds the row
-  // with group-major index L = 32*g + 4*rt + i, i.e. token L / H, head L % H.
-  // A lane group then holds whole tokens (H <= 32: TPL tokens per lane, no
-  // cross-lane sum) or 1/GPT of one token (H = 64, 128: GPT lane groups are
+  // with group-major index L = GR*g + 4*rt + i, i.e. token L / H, head L % H.
+  // A lane group then holds whole tokens (H <= GR: TPL tokens per lane, no
+  // cross-lane sum) or 1/GPT of one token (H > GR: GPT lane groups are
   // summed with 1 or 2 lane swaps).
-  static constexpr int TPL = H < 32 ? 32 / H : 1;  // tokens per lane
-  static constexpr int GPT = H > 32 ? H / 32 : 1;  // lane groups per token
+  static constexpr int TPL = H < GR ? GR / H : 1;  // tokens per lane
+  static constexpr int GPT = H > GR ? H / GR : 1;  // lane groups per token
 };
 
 // Sum of v over the lanes l and l^16 (S = 16) or l and l^32 (S = 32), using
@@ -138,14 +143,14 @@ __device__ __forceinline__ int tile_off(int kk, int c) {
   return kk * D + ((c ^ (kk % CPR)) << 4);
 }
 
-template <int H, int D, bool KP>
+template <int H, int D, bool KP, int RT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int* __restrict__ ks,
     const int* __restrict__ ke, float* __restrict__ logits, int M, int N, int B,
     int n_tblocks, int n_chunks, int chunk_keys) {
-  using C = IdxCfg<H, D, KP>;
+  using C = IdxCfg<H, D, KP, RT>;
   static_assert(!KP || (C::KT / 16) % kIdxWaves == 0, "key-parallel: whole sub-tiles per wave");
   static_assert(C::KT <= kIdxThreads, "one key scale per thread");
   __shared__ __align__(16) uint8_t sK[2][C::TILE_BYTES];
@@ -162,12 +167,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   // ---- this wave's tokens: q fragments and effective weights (issued
   // before the window reduction, which they do not depend on) ------------
   const int tw0 = KP ? t0 : t0 + wave * C::TW;
-  i32x8 qf[kRT][C::KS];
-  float weff[kRT][4], qsc[kRT][4];
+  i32x8 qf[RT][C::KS];
+  float weff[RT][4], qsc[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     // A row col of tile rt is C row (g', i') = (col / 4, col % 4)
-    const int L = 32 * (col >> 2) + 4 * rt + (col & 3);
+    const int L = C::GR * (col >> 2) + 4 * rt + (col & 3);
     const int t = tw0 + L / H, h = L % H;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int L2 = 32 * g + 4 * rt + i;
+      const int L2 = C::GR * g + 4 * rt + i;
       const int t2 = tw0 + L2 / H, h2 = L2 % H;
       float we = 0.f, qs = 1.f;
       if (t2 < M) {
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   float* orow[C::TPL];
 #pragma unroll
   for (int j = 0; j < C::TPL; ++j) {
-    const int t = tw0 + (32 * g) / H + j;
+    const int t = tw0 + (C::GR * g) / H + j;
     int s = 0, e = 0;
     if (t < M) {
       const int r = b * M + t;
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   const bool store_lane = (g % C::GPT) == 0;
 
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) weff[rt][i] *= qsc[rt][i];
 
@@ -324,11 +329,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       // 16-key sub-tiles, software pipelined (128-deep keys): the MFMAs of
       // sub-tile n+1 are issued before the epilogue of sub-tile n
       constexpr int NB = C::KS == 1 ? 2 : 1;
-      f32x4 acc[NB][kRT];
+      f32x4 acc[NB][RT];
       auto mm = [&](int n, f32x4* a) {
         const int kk = n * 16 + col;
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) a[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) a[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
           i32x8 bf = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
             bf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) a[rt] = mfma_f8_16x16x128(qf[rt][s], bf, a[rt]);
+          for (int rt = 0; rt < RT; ++rt) a[rt] = mfma_f8_16x16x128(qf[rt][s], bf, a[rt]);
         }
       };
       // epilogue: relu * weight, sum over heads, * k_scale (epi_sum), masked
@@ -352,11 +357,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) part[j][i] = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            part[(4 * rt + i) / (32 / C::TPL)][i] =
-                fmaf(relu(a[rt][i]), weff[rt][i], part[(4 * rt + i) / (32 / C::TPL)][i]);
+            part[(4 * rt + i) / (C::GR / C::TPL)][i] =
+                fmaf(relu(a[rt][i]), weff[rt][i], part[(4 * rt + i) / (C::GR / C::TPL)][i]);
 #pragma unroll
         for (int j = 0; j < C::TPL; ++j) sum[j] = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
         if constexpr (C::GPT >= 2) sum[0] = lane_swap_sum<16>(sum[0]);
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
             // epilogue, which the fp8 MFMA (32 cycles) hides
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
 #pragma unroll
-            for (int i = 0; i < kRT * C::KS; ++i) {
+            for (int i = 0; i < RT * C::KS; ++i) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
               __builtin_amdgcn_sched_group_barrier(0x002, kIdxVpm, 0);  // VALU
             }
@@ -440,9 +445,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   }
 }
 
-template <int H, int D, bool KP>
+template <int H, int D, bool KP, int RT = kRT>
 hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
-  using C = IdxCfg<H, D, KP>;
+  using C = IdxCfg<H, D, KP, RT>;
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
   // Key chunks: a chunk reloads its token block's q, so blocks are split
   // only as far as needed to give every workgroup slot of the device an item
@@ -467,16 +472,20 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   const long long items = tblocks * n_chunks;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const long long blocks = KP ? items : (items < slots ? items : slots);
-  hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
+  hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP, RT>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
                      stream, (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                      a.ks, a.ke, a.logits, (int)a.M, (int)a.N, (int)a.B, n_tblocks, n_chunks,
                      chunk_keys);
   return hipGetLastError();
 }
 
-// Few tokens per batch entry (decode): the key-parallel layout.
+// Few tokens per batch entry (decode): the key-parallel layout; one token
+// per batch entry with fewer than 128 heads: H / 16 row tiles, no empty rows.
 template <int H, int D>
 hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
+  if constexpr (H >= 16 && H < kRowsPerWave) {
+    if (a.M == 1) return launch_kp<H, D, true, H / 16>(a, stream);
+  }
   if (a.M * H <= kRowsPerWave) return launch_kp<H, D, true>(a, stream);
   return launch_kp<H, D, false>(a, stream);
 }

@@ -57,6 +57,27 @@ def test_indexer_no_q_scale_and_one_token():
     check_logits(g, ref, terms, "no q_scale")
 
 
+@pytest.mark.parametrize("H,D,M", [(16, 128, 1), (32, 64, 1), (64, 128, 1), (64, 256, 1),
+                                   (128, 128, 1), (64, 128, 2), (4, 64, 16)])
+def test_indexer_decode_layouts(H, D, M):
+    """Key-parallel layouts: one token per batch entry (H / 16 row tiles per
+    wave) and a few tokens sharing a wave's 128 rows; windows of any length
+    in several key chunks, empty and past-the-end ones included."""
+    wl = _small(H, D, M=M, N=5000, B=5, seed=H + D + M)
+    log(f"indexer decode layout H={H} D={D} M={M}")
+    x = W.make_inputs(wl, parts=("indexer",))
+    rng = np.random.default_rng(H * 7 + M)
+    ks = rng.integers(-20, 200, (wl.B, wl.M)).astype(np.int32)
+    ke = rng.integers(0, wl.N + 50, (wl.B, wl.M)).astype(np.int32)
+    ks[0, 0], ke[0, 0] = 0, wl.N
+    ks[1, 0], ke[1, 0] = 300, 300  # empty
+    x["ks"], x["ke"] = ks, ke
+    g = indexer_gpu(x, wl.N).cpu().numpy().reshape(-1, wl.N)
+    ref, terms = oracle.indexer_logits(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"],
+                                       ks, ke, with_terms=True)
+    check_logits(g, ref, terms, f"decode H{H}D{D}M{M}")
+
+
 WORKLOAD_ROWS = {"tiny_causal_256": None, "prefill_4096": 40, "varlen_4x8192": 24,
                  "decode_b64": 12, "prefill_8192_fp8kv": 24}
 
