@@ -168,7 +168,7 @@ template <int DQK, int DV, bool FP8, int NW, int HPW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_, const float* __restrict__ kv_scale,
     const float* __restrict__ sink, const int* __restrict__ idx, uint16_t* __restrict__ o, int M,
-    int N, int Hq, int K, float scale_log2, int S, int kspan, float* __restrict__ wso,
+    int N, int Hq, int K, float scale_log2, int S, int kspan, uint16_t* __restrict__ wso,
     float2* __restrict__ wsml) {
   using C = AttnCfg<DQK, DV, FP8, NW, HPW>;
   constexpr int HT = C::HT, PG = C::PG, OH = C::OH, OTW = C::OTW;
@@ -668,14 +668,22 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     }
   }
   if constexpr (SPLIT) {
-    // split: unnormalised O, and (m, l) of each head, for the merge kernel
+    // split: this split's normalised O in bf16 (O / l; 0 without a valid
+    // index) and (m, l) of each head, for the merge kernel
     const size_t part = (size_t)rtok * S + split;
 #pragma unroll
     for (int oh = 0; oh < OH; ++oh) {
       const int h = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 + col;
-      float* orow = wso + (part * Hq + h) * DV + c0 + g * 4;
+      uint16_t* orow = wso + (part * Hq + h) * DV + c0 + g * 4;
+      const float inv = lf[oh] > 0.f ? __builtin_amdgcn_rcpf(lf[oh]) : 0.f;
 #pragma unroll
-      for (int t = 0; t < OTW; ++t) *reinterpret_cast<f32x4*>(orow + t * 16) = oacc[oh][t];
+      for (int t = 0; t < OTW; ++t) {
+        const f32x4 v = oacc[oh][t];
+        uint2 pk2;
+        pk2.x = pack_bf16x2(v[0] * inv, v[1] * inv);
+        pk2.y = pack_bf16x2(v[2] * inv, v[3] * inv);
+        *reinterpret_cast<uint2*>(orow + t * 16) = pk2;
+      }
       if (g == 0 && wave % PG == 0) wsml[part * Hq + h] = float2{mf[oh], lf[oh]};
     }
   } else {
@@ -734,7 +742,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 // with M = max_s m_s -- the same value as one pass over all K indices,
 // since every split's O_s and l_s share its reference m_s.
 template <int DV>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ wso,
+__global__ __launch_bounds__(256) void attn_merge_kernel(const uint16_t* __restrict__ wso,
                                                          const float2* __restrict__ wsml,
                                                          const float* __restrict__ sink,
                                                          uint16_t* __restrict__ o, int Hq, int S) {
@@ -752,9 +760,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) {
     const float2 ml = wsml[(p0 + s) * Hq + h];
-    const float wgt = fast_exp2(ml.x - mmax);
-    l += wgt * ml.y;
-    acc += wgt * *reinterpret_cast<const f32x4*>(wso + ((p0 + s) * Hq + h) * DV + cq);
+    const float wgt = fast_exp2(ml.x - mmax) * ml.y;  // the split's share of l
+    l += wgt;
+    const uint2 pk = *reinterpret_cast<const uint2*>(wso + ((p0 + s) * Hq + h) * DV + cq);
+    acc += wgt * f32x4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xffff0000u),
+                       __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xffff0000u)};
   }
   if (sink) l += fast_exp2(sink[h] * kLog2e - mmax);
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -797,7 +807,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   void* ws = nullptr;
   if (S > 1) {
     keep_pool_memory();
-    const size_t bytes = (size_t)rows * S * a.Hq * (DV * sizeof(float) + sizeof(float2));
+    const size_t bytes = (size_t)rows * S * a.Hq * (DV * sizeof(uint16_t) + sizeof(float2));
     if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) {
       (void)hipGetLastError();
       ws = nullptr;
@@ -805,7 +815,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
       kspan = a.K;
     }
   }
-  float* wso = static_cast<float*>(ws);
+  uint16_t* wso = static_cast<uint16_t*>(ws);
   float2* wsml = ws ? reinterpret_cast<float2*>(wso + (size_t)rows * S * a.Hq * DV) : nullptr;
   if (ws)
     hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, true>),
