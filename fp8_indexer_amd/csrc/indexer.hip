@@ -42,7 +42,7 @@ constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
 #endif
 constexpr int kKT = DSA_IDX_KT;                 // keys per LDS tile (tuning knob)
 constexpr int kXcds = 8;
-constexpr int kMinChunk = 512;  // keys per chunk, at least
+constexpr int kMinChunk = 64;   // keys per chunk, at least (one key tile)
 // VALU instructions scheduled after each MFMA of the next sub-tile (tuning knob)
 #ifndef DSA_IDX_VPM
 #define DSA_IDX_VPM 10
@@ -451,7 +451,8 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   const int n_tblocks = (int)((a.M + C::TB - 1) / C::TB);
   // Key chunks: a chunk reloads its token block's q, so blocks are split
   // only as far as needed to give every workgroup slot of the device an item
-  // (decode-like inputs with few token blocks), with chunks of >= 512 keys.
+  // (decode-like and small inputs with few token blocks), with chunks of at
+  // least one key tile.
   // The persistent layout wants two items per workgroup, so that the snake
   // schedule can pair long windows with short ones.
   int cus = 256;
