@@ -18,8 +18,10 @@
  *    waits for its kernels and reports their errors.
  *  * Ownership: the caller allocates and owns every buffer, including the
  *    intermediates of dsa_prefill.  The library keeps no pointer after a call
- *    returns.  The only device memory it takes is the stream-ordered
- *    temporary of dsa_sparse_attn_fwd (and dsa_prefill) for few query rows,
+ *    returns.  The only device memory it takes are stream-ordered
+ *    temporaries (hipMallocAsync / hipFreeAsync on the call's stream, from
+ *    the device's default memory pool): dsa_topk's when N > 8192 and
+ *    dsa_sparse_attn_fwd's for few query rows (also inside dsa_prefill),
  *    described there.  Calls are thread-safe.
  *  * Errors: arguments are checked on the host before anything is enqueued.
  *    NULL pointers, non-positive sizes, misalignment or inconsistent sizes
@@ -106,6 +108,12 @@ dsa_status dsa_indexer_logits(const void* q, const float* q_scale,
  *   ks, ke     [B, M]    int32
  *   topk_idxs  [B, M, K] int32 output
  * Supported: 1 <= K <= 4096, N < 2^31.  Output is deterministic.
+ * Temporaries (N > 8192 only): with fewer than 256 rows, every row is cut
+ * into 4096-key segments that share per-row digit histograms,
+ * B*M*(6144 + ceil(N/4096)*1028)*4 bytes; with more rows, longer windows
+ * go through a candidate buffer of B*M*ceil(N/8192)*K*4 bytes when that is
+ * at most 256 MiB.  If an allocation fails (or the buffer would be larger),
+ * a path without temporaries gives the same result.
  */
 dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
                     int32_t* topk_idxs, int64_t B, int64_t M, int64_t N,
@@ -139,7 +147,7 @@ dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
  * decode): each row's K indices are split over several workgroups whose
  * partial results are merged by a second kernel; the partials live in a
  * temporary taken with hipMallocAsync on `stream` from the device's default
- * memory pool (B*M*splits*Hq*(4*Dv + 8) bytes, splits <= K/128) and freed
+ * memory pool (B*M*splits*Hq*(2*Dv + 8) bytes, splits <= K/128) and freed
  * with hipFreeAsync on the same stream.  If that allocation fails, the rows
  * run unsplit with the same result.
  */
