@@ -112,18 +112,22 @@ def test_attn_workloads(name):
     log(f"  max|d| {mx:.3g} mean|d| {mn:.3g}")
 
 
+@pytest.mark.parametrize("Hq", [128, 64])
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("where", ["middle", "last", "first", "moderate"])
-def test_attn_reference_restart(fp8, where):
+@pytest.mark.parametrize("where", ["middle", "last", "first", "moderate", "second_half"])
+def test_attn_reference_restart(fp8, where, Hq):
     """A score far above every score of the first tile (the kernel's fixed
     softmax reference: 72 natural units, p ~ 2^104) forces the max-only
     pre-pass and the second pass.  "moderate": ~21 natural units above (p ~
-    2^30), which the fixed reference carries exactly without a restart."""
+    2^30), which the fixed reference carries exactly without a restart.
+    "second_half": the big score in rows 16-31 of the first tile (with 64
+    heads the other key half's waves, whose maximum sets the shared
+    reference)."""
     B, M, N, K = 1, 2, 600, 256
-    wl = W.Workload("r", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, kv_fp8=fp8,
+    wl = W.Workload("r", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
                     seed=6)
     x = W.make_inputs(wl, parts=("attn",))
-    big = {"middle": 300, "last": 599, "first": 3, "moderate": 300}[where]
+    big = {"middle": 300, "last": 599, "first": 3, "moderate": 300, "second_half": 301}[where]
     qv = torch.ones((B, M, wl.Hq, wl.Dqk), dtype=torch.float32) * 0.5
     qv[..., ::2] = 1.0
     x["q"] = qv.to(torch.bfloat16)
@@ -140,22 +144,23 @@ def test_attn_reference_restart(fp8, where):
         x["kv"] = kvf.to(torch.bfloat16)
     idx = np.tile(np.arange(0, 2 * K, 2, dtype=np.int32), (B, M, 1))  # rows 0,2,..,510
     idx[0, 0, K // 2] = big
-    idx[0, 1, 0 if where == "first" else K - 1] = big
+    idx[0, 1, {"first": 0, "second_half": 20}.get(where, K - 1)] = big
     o = _run(x, idx, wl)
     ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
                              kv_scale=x["kv_scale"])
     check_attn(o, ref, f"restart/{where}")
 
 
+@pytest.mark.parametrize("Hq", [128, 64])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_attn_split_rows_edge_cases(fp8):
+def test_attn_split_rows_edge_cases(fp8, Hq):
     """Few rows with K = 2048: each row's indices are split over several
     workgroups and merged.  Row 0 has no valid index (zero output), row 1
     only valid indices in the last split, row 2 a full set."""
     B, M, N, K = 1, 3, 5000, 2048
-    wl = W.Workload("s", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, kv_fp8=fp8,
+    wl = W.Workload("s", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
                     seed=9)
-    log(f"attn split edge fp8={fp8}")
+    log(f"attn split edge fp8={fp8} Hq={Hq}")
     x = W.make_inputs(wl, parts=("attn",))
     rng = np.random.default_rng(5)
     idx = np.full((B, M, K), -1, np.int32)
