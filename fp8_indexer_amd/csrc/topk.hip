@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   __shared__ uint32_t hist[4096];
   __shared__ int sWave[kTkWaves];
   __shared__ int sCnt[2][kTkWaves];
-  __shared__ int sSel[2];
+  __shared__ int sSel[3];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t r = blockIdx.x;
@@ -253,10 +253,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 // One MSD round's threshold: hist[0..nb) counts the remaining keys by digit
 // (larger digit = larger key); returns the digit bin holding the krem-th
-// largest of them and the number of keys in the bins above it.  Called by
-// every thread of a kRowThreads workgroup; hist may be in LDS or in global
-// memory.
-__device__ __forceinline__ int2 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
+// largest of them (x), the number of keys in the bins above it (y) and the
+// bin's own count (z).  Called by every thread of a kRowThreads workgroup;
+// hist may be in LDS or in global memory; sSel holds 3 ints.
+__device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
                                               int* sSel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bpt = nb / kRowThreads;  // bins per thread
@@ -279,12 +279,13 @@ __device__ __forceinline__ int2 threshold_bin(const uint32_t* hist, int nb, int 
       if (above < krem && krem <= above + c) {
         sSel[0] = tid * bpt + j;
         sSel[1] = above;
+        sSel[2] = c;
       }
       above += c;
     }
   }
   __syncthreads();
-  return make_int2(sSel[0], sSel[1]);
+  return make_int3(sSel[0], sSel[1], sSel[2]);
 }
 
 // Digit layout of the 32-bit key: rounds of 11, 11 and 10 bits.
@@ -365,35 +366,47 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
     keys[c] = i < len ? order_key(GATHER ? src[cand[i]] : src[i]) : 0u;
   }
 
+  // After a round whose threshold bin holds exactly the keys still needed,
+  // every key of that bin is selected, so the keys >= its smallest key (the
+  // remaining digits zero) are exactly the K: the later rounds are skipped
+  // (uniformly: the decision comes from LDS) and every key equal to that
+  // bound is taken.  Only with up to 16 keys per lane: with 32 the extra
+  // state costs registers, hence occupancy, which the long rows need more.
+  constexpr bool kEarly = KR <= 16;
   uint32_t prefix = 0;
-  int krem = K, above_total = 0;
+  int krem = K, above_total = 0, low_bits = 0;
 #pragma unroll
   for (int round = 0; round < 3; ++round) {
     const int bits = digit_bits(round), shift = digit_shift(round);
-    const int nb = 1 << bits;
-    for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
-    __syncthreads();
+    if (!kEarly || low_bits == 0) {
+      const int nb = 1 << bits;
+      for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+      __syncthreads();
 #pragma unroll
-    for (int c = 0; c < KR; ++c) {
-      if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
-      const int i = base + c * kWave + lane;
-      const uint32_t u = keys[c];
-      if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
-        atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+      for (int c = 0; c < KR; ++c) {
+        if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
+        const int i = base + c * kWave + lane;
+        const uint32_t u = keys[c];
+        if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
+          atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      const int3 sel = threshold_bin(hist, nb, krem, sRed, sSel);
+      prefix = (prefix << bits) | (uint32_t)sel.x;
+      krem -= sel.y;
+      above_total += sel.y;
+      if (kEarly && sel.z == krem) low_bits = shift;
     }
-    __syncthreads();
-    const int2 sel = threshold_bin(hist, nb, krem, sRed, sSel);
-    prefix = (prefix << bits) | (uint32_t)sel.x;
-    krem -= sel.y;
-    above_total += sel.y;
   }
-  emit_selected<KR, GATHER>(keys, len, prefix, K - above_total, 0, 0, first, cand, K, o, sCnt);
+  const uint32_t tau = kEarly ? prefix << low_bits : prefix;
+  const int n_eq = kEarly && low_bits ? K : K - above_total;
+  emit_selected<KR, GATHER>(keys, len, tau, n_eq, 0, 0, first, cand, K, o, sCnt);
 }
 
 #define DSA_TOPK_LDS                                  \
   __shared__ __align__(16) uint32_t hist[2048];       \
   __shared__ int sRed[kRowWaves];                     \
-  __shared__ int sSel[2];                             \
+  __shared__ int sSel[3];                             \
   __shared__ int sCnt[2][kRowWaves];
 
 template <int KR>
@@ -540,7 +553,7 @@ __device__ __forceinline__ void split_prefix(const uint32_t* h, int nr, int K, u
   prefix = 0;
   above = 0;
   for (int q = 0; q < nr; ++q) {
-    const int2 sel = threshold_bin(h + q * 2048, 1 << digit_bits(q), K - above, sRed, sSel);
+    const int3 sel = threshold_bin(h + q * 2048, 1 << digit_bits(q), K - above, sRed, sSel);
     prefix = (prefix << digit_bits(q)) | (uint32_t)sel.x;
     above += sel.y;
   }
@@ -554,7 +567,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_round_kernel(
     uint32_t* __restrict__ ws, int N, int K, int nseg) {
   __shared__ uint32_t lh[2048];
   __shared__ int sRed[kRowWaves];
-  __shared__ int sSel[2];
+  __shared__ int sSel[3];
   constexpr int bits = digit_bits(ROUND), shift = digit_shift(ROUND), nb = 1 << bits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   size_t r;
@@ -624,7 +637,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
     const float* __restrict__ logits, const int* __restrict__ ks, const int* __restrict__ ke,
     const uint32_t* __restrict__ ws, int* __restrict__ out, int N, int K, int nseg) {
   __shared__ int sRed[kRowWaves];
-  __shared__ int sSel[2];
+  __shared__ int sSel[3];
   __shared__ int sCnt[2][kRowWaves];
   size_t r;
   int s0;
