@@ -61,6 +61,29 @@ def test_prefill_exact_arithmetic(name, M, K):
     check_attn(o, ro, name)
 
 
+def test_prefill_exact_arithmetic_decode():
+    """Decode shapes through every path they take: one token per batch
+    entry (the indexer's one-token layout), windows past 8192 keys with few
+    rows (the top-k split into segments), few rows (attention split over
+    workgroups with bf16 partials and a merge).  Exact logits, so the top-k
+    must match exactly."""
+    wl = W.WORKLOADS["decode_b64"].with_(B=6, N=20000, K=256, decode_min=300)
+    log(f"prefill exact-arithmetic decode B={wl.B} N={wl.N} K={wl.K}")
+    x = _exact_inputs(wl, seed=4)
+    logits, idx, o = _prefill(x, wl)
+    R = wl.B * wl.M
+    ref = oracle.indexer_logits(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["ks"],
+                                x["ke"])
+    g = logits.cpu().numpy().reshape(R, wl.N)
+    win = ~np.isnan(ref)
+    assert np.array_equal(g[win], ref[win]), "exact logits differ"
+    ti = oracle.topk(ref, x["ks"], x["ke"], wl.B, wl.M, wl.N, wl.K)
+    assert np.array_equal(idx.cpu().numpy().reshape(R, wl.K), ti), "top-k differs"
+    ro = oracle.sparse_attn(x["q"], x["kv"], x["sink"], ti.reshape(wl.B, wl.M, wl.K),
+                            wl.sm_scale, wl.Dv, kv_scale=x["kv_scale"])
+    check_attn(o, ro, "decode")
+
+
 def _topk_properties(lg, ks, ke, idx, K):
     """Valid exact top-k of the given rows: ascending, in window, right count,
     every selected value >= every unselected one, ties to the lower index."""
