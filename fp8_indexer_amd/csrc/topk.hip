@@ -19,13 +19,17 @@
 //
 // Rows whose window has up to 8192 keys: one 256-thread workgroup per row,
 // each wave holding a contiguous quarter of the row in VGPRs (digits of 11,
-// 11 and 10 bits, a shared LDS histogram, wave-level scans).  The path is
-// chosen per row from its own window, not from N: longer windows (only
-// possible when N > 8192) are left to a second launch, which cuts them into
-// 8192-key segments and reduces the segments' candidates, or, when that
-// launch's candidate buffer would be large, gives each row one 512-thread
-// workgroup that re-reads the row from L2 on each pass (digits 12, 10, 10).
-// Rows with len <= K only write s..e-1 and -1 padding.
+// 11 and 10 bits, a shared LDS histogram, wave-level scans; with up to 4096
+// keys the rounds stop early once the threshold bin is wholly selected).
+// The path is chosen per row from its own window, not from N: longer
+// windows (only possible when N > 8192) are left to a second launch, which
+// cuts them into 8192-key segments and reduces the segments' candidates, or,
+// when that launch's candidate buffer would be large, gives each row one
+// 512-thread workgroup that re-reads the row from L2 on each pass (digits
+// 12, 10, 10).  With few rows and N > 8192 every row is instead cut into
+// 4096-key segments that share per-row digit histograms in global memory
+// (one launch per round).  Rows with len <= K only write s..e-1 and -1
+// padding.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
