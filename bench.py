@@ -104,8 +104,8 @@ def cpu_baseline(wl, x, budget_s):
         dt = run(rows)
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} of {R} query rows, evenly spaced over the 4096-token "
-                      f"causal prefill (indexer -> top-k -> attention, fp64 C oracle), "
+            "sample": f"{len(rows)} of {R} query rows, evenly spaced over the {wl.name} "
+                      f"workload (indexer -> top-k -> attention, fp64 C oracle), "
                       f"{dt:.1f} s"}
 
 
@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="steps timed with L2/MALL flushed before each (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", default="prefill_4096",
+                    help="workload to time (default: the 4096-token causal prefill)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -148,7 +150,7 @@ def main():
     import fp8_indexer_amd as dsa
     import workloads as W
 
-    wl = W.WORKLOADS["prefill_4096"]
+    wl = W.WORKLOADS[args.workload]
     eprint(f"[bench] generating inputs for {wl.name}")
     x = W.make_inputs(wl)
     dev = torch.device("cuda:0")
@@ -172,7 +174,8 @@ def main():
         dsa.topk(logits, g["ks"], g["ke"], wl.K, out=idx)
         if ev:
             ev[-2].record(stream)
-        dsa.sparse_attn_fwd(g["q"], g["kv"], g["sink"], idx, wl.sm_scale, wl.Dv, out=o)
+        dsa.sparse_attn_fwd(g["q"], g["kv"], g["sink"], idx, wl.sm_scale, wl.Dv, out=o,
+                            kv_scale=g.get("kv_scale"))
         if ev:
             ev[-1].record(stream)
 
@@ -223,7 +226,7 @@ def main():
         e0.record(stream)
         dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
                     wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
-                    logits=logits, topk_idxs=idx, out=o)
+                    logits=logits, topk_idxs=idx, out=o, kv_scale=g.get("kv_scale"))
         e1.record(stream)
         torch.cuda.synchronize()
         pf.append(e0.elapsed_time(e1))
@@ -234,13 +237,13 @@ def main():
     for _ in range(2):
         dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
                     wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
-                    logits=logits, topk_idxs=idx, out=o)
+                    logits=logits, topk_idxs=idx, out=o, kv_scale=g.get("kv_scale"))
     torch.cuda.synchronize()
     tp0 = time.perf_counter()
     for _ in range(args.steps):
         dsa.prefill(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
                     wl.K, g["q"], g["kv"], g["sink"], sm_scale=wl.sm_scale, dv=wl.Dv,
-                    logits=logits, topk_idxs=idx, out=o)
+                    logits=logits, topk_idxs=idx, out=o, kv_scale=g.get("kv_scale"))
     torch.cuda.synchronize()
     ms_prefill = (time.perf_counter() - tp0) * 1e3 / args.steps
 
@@ -251,7 +254,7 @@ def main():
     topk_gbs = wc["topk_bytes"] / (ms_topk * 1e-3) / 1e9
     roof_s = (wc["idx_flops"] / (PEAK_FP8_TFLOPS * 1e12) + wc["topk_bytes"] / (PEAK_HBM_GBS * 1e9)
               + wc["att_flops"] / (PEAK_BF16_TFLOPS * 1e12))
-    traffic = load_traffic()
+    traffic = load_traffic() if wl.name == "prefill_4096" else None
     res = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -268,7 +271,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "seq_len": M, "index_heads": wl.H,
                    "index_dim": wl.D, "topk": wl.K, "heads": wl.Hq, "dqk": wl.Dqk, "dv": wl.Dv,
-                   "kv": "bf16", "windows": "causal"},
+                   "kv": "fp8_e4m3fn" if wl.kv_fp8 else "bf16", "windows": wl.windows},
         "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel",
                      "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": att_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
