@@ -9,6 +9,15 @@ built, every call raises.
     idx    = topk(logits, ks, ke, K)
     o      = sparse_attn_fwd(q, kv, attn_sink, idx, sm_scale, dv)
     logits, idx, o = prefill(...)
+
+Shapes, dtypes, contiguity and devices of every tensor are checked here
+before the C call (the C ABI sees pointers only and cannot): a mismatch
+raises ValueError (shape) or TypeError (dtype, device).
+
+`workspace` (top-k, attention, prefill): "auto" (default) takes the device
+scratch the call's fastest path needs from torch's caching allocator on the
+current stream; None runs the paths that need no scratch; a contiguous
+uint8 CUDA tensor is used as given.
 """
 import ctypes
 import os
@@ -16,13 +25,13 @@ import os
 import torch
 
 __all__ = ["DSAError", "lib", "version", "indexer_logits", "topk", "sparse_attn_fwd",
-           "prefill", "KV_BF16", "KV_FP8_E4M3FN", "LIB_PATH"]
+           "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
+           "prefill_workspace_size", "KV_BF16", "KV_FP8_E4M3FN", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 KV_BF16, KV_FP8_E4M3FN = 0, 1
-_STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_VALUE", 2: "DSA_ERR_NOT_SUPPORTED",
-           3: "DSA_ERR_LAUNCH"}
-EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_attn_fwd", "dsa_prefill",
+EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
+           "dsa_sparse_attn_workspace_size", "dsa_prefill", "dsa_prefill_workspace_size",
            "dsa_status_string", "dsa_version")
 
 
@@ -46,6 +55,7 @@ class PrefillArgs(ctypes.Structure):
         ("heads", ctypes.c_int32), ("dqk", ctypes.c_int32), ("dv", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("logits", ctypes.c_void_p), ("topk_idxs", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -59,14 +69,21 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m fp8_indexer_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
-        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        psz = ctypes.POINTER(ctypes.c_size_t)
         L.dsa_indexer_logits.restype = ctypes.c_int
         L.dsa_indexer_logits.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, P]
+        L.dsa_topk_workspace_size.restype = ctypes.c_int
+        L.dsa_topk_workspace_size.argtypes = [i64, i64, i64, i32, psz]
         L.dsa_topk.restype = ctypes.c_int
-        L.dsa_topk.argtypes = [P, P, P, P, i64, i64, i64, i32, P]
+        L.dsa_topk.argtypes = [P, P, P, P, i64, i64, i64, i32, P, sz, P]
+        L.dsa_sparse_attn_workspace_size.restype = ctypes.c_int
+        L.dsa_sparse_attn_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, psz]
         L.dsa_sparse_attn_fwd.restype = ctypes.c_int
         L.dsa_sparse_attn_fwd.argtypes = [P, P, ctypes.c_int, P, P, P, P, i64, i64, i64, i32,
-                                          i32, i32, i32, ctypes.c_float, P]
+                                          i32, i32, i32, ctypes.c_float, P, sz, P]
+        L.dsa_prefill_workspace_size.restype = ctypes.c_int
+        L.dsa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs), psz]
         L.dsa_prefill.restype = ctypes.c_int
         L.dsa_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -89,98 +106,170 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t, name, dtypes):
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_BF16 = (torch.bfloat16,)
+
+
+def _tensor(t, name, dtypes, shape):
+    """dtype, contiguity and shape of one argument (None passes)."""
     if t is None:
-        return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return t
 
 
-_FP8 = (torch.float8_e4m3fn, torch.uint8)
+def _rank(t, name, n):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name}: expected {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _same_device(ref, *ts):
+    """Every given tensor is a CUDA (HIP) tensor on ref's device."""
+    if not ref.is_cuda:
+        raise TypeError("tensors must be CUDA (HIP) tensors")
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise TypeError(f"all tensors must be on {ref.device}, found one on {t.device}")
 
 
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _workspace(workspace, nbytes, device):
+    """(pointer, size) of the scratch to pass: see the module docstring."""
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        if nbytes == 0:
+            return None, 0, None
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return ctypes.c_void_p(buf.data_ptr()), nbytes, buf
+    _tensor(workspace, "workspace", (torch.uint8,), (workspace.numel(),))
+    if workspace.device != device:
+        raise TypeError(f"workspace must be on {device}")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), workspace
+
+
+def topk_workspace_size(B, M, N, K):
+    """Bytes of scratch dsa_topk's fastest path needs (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check("dsa_topk_workspace_size", lib().dsa_topk_workspace_size(B, M, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_workspace_size(B, M, Hq, Dqk, Dv, K):
+    """Bytes of scratch dsa_sparse_attn_fwd's fastest path needs on the
+    current device (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check("dsa_sparse_attn_workspace_size",
+           lib().dsa_sparse_attn_workspace_size(B, M, Hq, Dqk, Dv, K, ctypes.byref(n)))
+    return n.value
+
+
 def indexer_logits(q, q_scale, k, k_scale, weights, ks, ke, logits=None):
     """logits [B,M,N] fp32 (entries outside each row's window are untouched)."""
-    _dev(q, "q", _FP8)
-    _dev(k, "k", _FP8)
-    _dev(q_scale, "q_scale", (torch.float32,))
-    _dev(k_scale, "k_scale", (torch.float32,))
-    _dev(weights, "weights", (torch.float32,))
-    _dev(ks, "ks", (torch.int32,))
-    _dev(ke, "ke", (torch.int32,))
-    B, M, H, D = q.shape
-    N = k.shape[1]
+    B, M, H, D = _rank(q, "q", 4)
+    N = _rank(k, "k", 3)[1]
+    _tensor(q, "q", _FP8, (B, M, H, D))
+    _tensor(k, "k", _FP8, (B, N, D))
+    _tensor(q_scale, "q_scale", _F32, (B, M, H))
+    _tensor(k_scale, "k_scale", _F32, (B, N))
+    _tensor(weights, "weights", _F32, (B, M, H))
+    _tensor(ks, "ks", _I32, (B, M))
+    _tensor(ke, "ke", _I32, (B, M))
+    _tensor(logits, "logits", _F32, (B, M, N))
+    _same_device(q, q_scale, k, k_scale, weights, ks, ke, logits)
     if logits is None:
         logits = torch.empty((B, M, N), dtype=torch.float32, device=q.device)
-    _dev(logits, "logits", (torch.float32,))
     _check("dsa_indexer_logits", lib().dsa_indexer_logits(
         _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(weights), _ptr(ks), _ptr(ke),
         _ptr(logits), B, M, N, H, D, _stream(q)))
     return logits
 
 
-def topk(logits, ks, ke, K, out=None):
+def topk(logits, ks, ke, K, out=None, workspace="auto"):
     """topk_idxs [B,M,K] int32: ascending selected indices, then -1."""
-    _dev(logits, "logits", (torch.float32,))
-    _dev(ks, "ks", (torch.int32,))
-    _dev(ke, "ke", (torch.int32,))
-    B, M, N = logits.shape
+    B, M, N = _rank(logits, "logits", 3)
+    _tensor(logits, "logits", _F32, (B, M, N))
+    _tensor(ks, "ks", _I32, (B, M))
+    _tensor(ke, "ke", _I32, (B, M))
+    _tensor(out, "out", _I32, (B, M, K))
+    _same_device(logits, ks, ke, out)
     if out is None:
         out = torch.empty((B, M, K), dtype=torch.int32, device=logits.device)
-    _dev(out, "out", (torch.int32,))
-    _check("dsa_topk", lib().dsa_topk(_ptr(logits), _ptr(ks), _ptr(ke), _ptr(out), B, M, N,
-                                      K, _stream(logits)))
+    need = topk_workspace_size(B, M, N, K) if isinstance(workspace, str) else 0
+    wp, wn, _keep = _workspace(workspace, need, logits.device)
+    _check("dsa_topk", lib().dsa_topk(_ptr(logits), _ptr(ks), _ptr(ke), _ptr(out), B, M, N, K,
+                                      wp, wn, _stream(logits)))
     return out
 
 
-def sparse_attn_fwd(q, kv, attn_sink, topk_idxs, sm_scale=0.0, dv=None, kv_scale=None, out=None):
+def sparse_attn_fwd(q, kv, attn_sink, topk_idxs, sm_scale=0.0, dv=None, kv_scale=None, out=None,
+                    workspace="auto"):
     """o [B,M,Hq,Dv] bf16.  kv is bf16, or e4m3fn codes with kv_scale [B,N]."""
-    _dev(q, "q", (torch.bfloat16,))
+    B, M, Hq, Dqk = _rank(q, "q", 4)
+    N = _rank(kv, "kv", 3)[1]
+    K = _rank(topk_idxs, "topk_idxs", 3)[2]
     fp8 = kv_scale is not None
-    _dev(kv, "kv", _FP8 if fp8 else (torch.bfloat16,))
-    _dev(kv_scale, "kv_scale", (torch.float32,))
-    _dev(attn_sink, "attn_sink", (torch.float32,))
-    _dev(topk_idxs, "topk_idxs", (torch.int32,))
-    B, M, Hq, Dqk = q.shape
-    N = kv.shape[1]
-    K = topk_idxs.shape[-1]
     dv = Dqk if dv is None else dv
+    _tensor(q, "q", _BF16, (B, M, Hq, Dqk))
+    _tensor(kv, "kv", _FP8 if fp8 else _BF16, (B, N, Dqk))
+    _tensor(kv_scale, "kv_scale", _F32, (B, N))
+    _tensor(attn_sink, "attn_sink", _F32, (Hq,))
+    _tensor(topk_idxs, "topk_idxs", _I32, (B, M, K))
+    _tensor(out, "out", _BF16, (B, M, Hq, dv))
+    _same_device(q, kv, kv_scale, attn_sink, topk_idxs, out)
     if out is None:
         out = torch.empty((B, M, Hq, dv), dtype=torch.bfloat16, device=q.device)
-    _dev(out, "out", (torch.bfloat16,))
-    _check("dsa_sparse_attn_fwd", lib().dsa_sparse_attn_fwd(
-        _ptr(q), _ptr(kv), KV_FP8_E4M3FN if fp8 else KV_BF16, _ptr(kv_scale), _ptr(attn_sink),
-        _ptr(topk_idxs), _ptr(out), B, M, N, Hq, Dqk, dv, K, float(sm_scale), _stream(q)))
+    with torch.cuda.device(q.device):  # the split count follows the device's CU count
+        need = (sparse_attn_workspace_size(B, M, Hq, Dqk, dv, K) if isinstance(workspace, str)
+                else 0)
+        wp, wn, _keep = _workspace(workspace, need, q.device)
+        _check("dsa_sparse_attn_fwd", lib().dsa_sparse_attn_fwd(
+            _ptr(q), _ptr(kv), KV_FP8_E4M3FN if fp8 else KV_BF16, _ptr(kv_scale),
+            _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, M, N, Hq, Dqk, dv, K,
+            float(sm_scale), wp, wn, _stream(q)))
     return out
 
 
-def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
-            attn_sink, sm_scale=0.0, dv=None, kv_scale=None, logits=None, topk_idxs=None,
-            out=None):
-    """The whole path on the current stream; returns (logits, topk_idxs, o)."""
-    for t, n, d in ((index_q, "index_q", _FP8), (index_k, "index_k", _FP8),
-                    (index_q_scale, "index_q_scale", (torch.float32,)),
-                    (index_k_scale, "index_k_scale", (torch.float32,)),
-                    (index_weights, "index_weights", (torch.float32,)),
-                    (ks, "ks", (torch.int32,)), (ke, "ke", (torch.int32,)),
-                    (q, "q", (torch.bfloat16,)), (attn_sink, "attn_sink", (torch.float32,)),
-                    (kv_scale, "kv_scale", (torch.float32,))):
-        _dev(t, n, d)
+def _prefill_args(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q,
+                  kv, attn_sink, sm_scale, dv, kv_scale, logits, topk_idxs, out):
+    """Checked dsa_prefill_args and the output tensors (allocated if None)."""
+    B, M, H, D = _rank(index_q, "index_q", 4)
+    N = _rank(index_k, "index_k", 3)[1]
+    Hq, Dqk = _rank(q, "q", 4)[2:]
     fp8 = kv_scale is not None
-    _dev(kv, "kv", _FP8 if fp8 else (torch.bfloat16,))
-    B, M, H, D = index_q.shape
-    N = index_k.shape[1]
-    _, _, Hq, Dqk = q.shape
     dv = Dqk if dv is None else dv
+    _tensor(index_q, "index_q", _FP8, (B, M, H, D))
+    _tensor(index_k, "index_k", _FP8, (B, N, D))
+    _tensor(index_q_scale, "index_q_scale", _F32, (B, M, H))
+    _tensor(index_k_scale, "index_k_scale", _F32, (B, N))
+    _tensor(index_weights, "index_weights", _F32, (B, M, H))
+    _tensor(ks, "ks", _I32, (B, M))
+    _tensor(ke, "ke", _I32, (B, M))
+    _tensor(q, "q", _BF16, (B, M, Hq, Dqk))
+    _tensor(kv, "kv", _FP8 if fp8 else _BF16, (B, N, Dqk))
+    _tensor(kv_scale, "kv_scale", _F32, (B, N))
+    _tensor(attn_sink, "attn_sink", _F32, (Hq,))
+    _tensor(logits, "logits", _F32, (B, M, N))
+    _tensor(topk_idxs, "topk_idxs", _I32, (B, M, K))
+    _tensor(out, "out", _BF16, (B, M, Hq, dv))
+    _same_device(q, index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, kv,
+                 kv_scale, attn_sink, logits, topk_idxs, out)
     dev = q.device
     if logits is None:
         logits = torch.empty((B, M, N), dtype=torch.float32, device=dev)
@@ -188,9 +277,6 @@ def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, k
         topk_idxs = torch.empty((B, M, K), dtype=torch.int32, device=dev)
     if out is None:
         out = torch.empty((B, M, Hq, dv), dtype=torch.bfloat16, device=dev)
-    _dev(logits, "logits", (torch.float32,))
-    _dev(topk_idxs, "topk_idxs", (torch.int32,))
-    _dev(out, "out", (torch.bfloat16,))
     a = PrefillArgs(
         batch=B, seq_q=M, seq_kv=N, index_q=index_q.data_ptr(),
         index_q_scale=index_q_scale.data_ptr() if index_q_scale is not None else None,
@@ -201,6 +287,29 @@ def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, k
         kv_scale=kv_scale.data_ptr() if fp8 else None,
         attn_sink=attn_sink.data_ptr() if attn_sink is not None else None,
         o=out.data_ptr(), heads=Hq, dqk=Dqk, dv=dv, sm_scale=float(sm_scale),
-        logits=logits.data_ptr(), topk_idxs=topk_idxs.data_ptr())
-    _check("dsa_prefill", lib().dsa_prefill(ctypes.byref(a), _stream(q)))
+        logits=logits.data_ptr(), topk_idxs=topk_idxs.data_ptr(), workspace=None,
+        workspace_bytes=0)
+    return a, logits, topk_idxs, out
+
+
+def prefill_workspace_size(args):
+    """Bytes of scratch dsa_prefill needs for a PrefillArgs (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check("dsa_prefill_workspace_size",
+           lib().dsa_prefill_workspace_size(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
+            attn_sink, sm_scale=0.0, dv=None, kv_scale=None, logits=None, topk_idxs=None,
+            out=None, workspace="auto"):
+    """The whole path on the current stream; returns (logits, topk_idxs, o)."""
+    a, logits, topk_idxs, out = _prefill_args(
+        index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
+        attn_sink, sm_scale, dv, kv_scale, logits, topk_idxs, out)
+    with torch.cuda.device(q.device):
+        need = prefill_workspace_size(a) if isinstance(workspace, str) else 0
+        wp, wn, _keep = _workspace(workspace, need, q.device)
+        a.workspace, a.workspace_bytes = (wp.value if wp is not None else None), wn
+        _check("dsa_prefill", lib().dsa_prefill(ctypes.byref(a), _stream(q)))
     return logits, topk_idxs, out

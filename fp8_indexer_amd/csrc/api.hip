@@ -2,6 +2,7 @@
 // argument validation, kernel dispatch, launch error mapping.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "dsa.h"
 #include "dsa_internal.h"
@@ -72,7 +73,50 @@ dsa_status check_attn(const void* q, const void* kv, int kv_dtype, const float* 
   return DSA_OK;
 }
 
+dsa_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr) return DSA_OK;  // paths without scratch
+  if (!aligned(ws, 16)) return DSA_ERR_INVALID_VALUE;
+  return ws_bytes < need ? DSA_ERR_WORKSPACE : DSA_OK;
+}
+
+dsa::AttnArgs attn_args(const void* q, const void* kv, int kv_dtype, const float* kv_scale,
+                        const float* sink, const int32_t* idx, void* o, int64_t B, int64_t M,
+                        int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K,
+                        float sm_scale) {
+  return dsa::AttnArgs{q, kv, kv_dtype == DSA_KV_FP8_E4M3FN, kv_scale, sink, idx, o, B, M,
+                       N, Hq, Dqk, Dv, K, sm_scale};
+}
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+namespace dsa {
+
+int device_cus() {
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  auto query = [dev] {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    return v;
+  };
+  if (dev < 0 || dev >= kMaxDevices) return query();
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) cache[dev] = query();
+  return cache[dev];
+}
+
+}  // namespace dsa
 
 extern "C" {
 
@@ -87,30 +131,63 @@ dsa_status dsa_indexer_logits(const void* q, const float* q_scale, const void* k
   return finish(dsa::launch_indexer(a, s), s);
 }
 
+dsa_status dsa_topk_workspace_size(int64_t B, int64_t M, int64_t N, int32_t K, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_VALUE;
+  const int32_t one = 0;
+  const dsa_status st = check_topk(reinterpret_cast<const float*>(&one), &one, &one, &one, B, M,
+                                   N, K);
+  if (st != DSA_OK) return st;
+  *bytes = dsa::topk_workspace_bytes(dsa::TopkArgs{nullptr, nullptr, nullptr, nullptr, B, M, N, K});
+  return DSA_OK;
+}
+
 dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke, int32_t* topk_idxs,
-                    int64_t B, int64_t M, int64_t N, int32_t K, void* stream) {
-  const dsa_status st = check_topk(logits, ks, ke, topk_idxs, B, M, N, K);
+                    int64_t B, int64_t M, int64_t N, int32_t K, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  dsa_status st = check_topk(logits, ks, ke, topk_idxs, B, M, N, K);
   if (st != DSA_OK) return st;
   dsa::TopkArgs a{logits, ks, ke, topk_idxs, B, M, N, K};
+  st = check_workspace(workspace, workspace_bytes, dsa::topk_workspace_bytes(a));
+  if (st != DSA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return finish(dsa::launch_topk(a, s), s);
+  return finish(dsa::launch_topk(a, dsa::Workspace{workspace, workspace_bytes}, s), s);
+}
+
+dsa_status dsa_sparse_attn_workspace_size(int64_t B, int64_t M, int32_t Hq, int32_t Dqk,
+                                          int32_t Dv, int32_t K, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_VALUE;
+  alignas(16) static const int64_t dummy[2] = {0, 0};  // stand-in pointers: never dereferenced
+  const dsa_status st = check_attn(dummy, dummy, DSA_KV_BF16, nullptr, nullptr,
+                                   reinterpret_cast<const int32_t*>(dummy), dummy, B, M, 1, Hq,
+                                   Dqk, Dv, K);
+  if (st != DSA_OK) return st;
+  *bytes = dsa::attn_workspace_bytes(
+      attn_args(nullptr, nullptr, DSA_KV_BF16, nullptr, nullptr, nullptr, nullptr, B, M, 1, Hq,
+                Dqk, Dv, K, 0.f));
+  return DSA_OK;
 }
 
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv, dsa_kv_dtype kv_dtype,
                                const float* kv_scale, const float* attn_sink,
                                const int32_t* topk_idxs, void* o, int64_t B, int64_t M, int64_t N,
                                int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K, float sm_scale,
-                               void* stream) {
-  const dsa_status st = check_attn(q, kv, (int)kv_dtype, kv_scale, attn_sink, topk_idxs, o, B, M,
-                                   N, Hq, Dqk, Dv, K);
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_attn(q, kv, (int)kv_dtype, kv_scale, attn_sink, topk_idxs, o, B, M, N,
+                             Hq, Dqk, Dv, K);
   if (st != DSA_OK) return st;
-  dsa::AttnArgs a{q,  kv, kv_dtype == DSA_KV_FP8_E4M3FN, kv_scale, attn_sink, topk_idxs, o, B, M,
-                  N,  Hq, Dqk, Dv, K, sm_scale};
+  const dsa::AttnArgs a = attn_args(q, kv, (int)kv_dtype, kv_scale, attn_sink, topk_idxs, o, B,
+                                    M, N, Hq, Dqk, Dv, K, sm_scale);
+  st = check_workspace(workspace, workspace_bytes, dsa::attn_workspace_bytes(a));
+  if (st != DSA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return finish(dsa::launch_attn(a, s), s);
+  return finish(dsa::launch_attn(a, dsa::Workspace{workspace, workspace_bytes}, s), s);
 }
 
-dsa_status dsa_prefill(const dsa_prefill_args* p, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status check_prefill(const dsa_prefill_args* p) {
   if (!p) return DSA_ERR_INVALID_VALUE;
   dsa_status st = check_indexer(p->index_q, p->index_q_scale, p->index_k, p->index_k_scale,
                                 p->index_weights, p->ks, p->ke, p->logits, p->batch, p->seq_q,
@@ -120,22 +197,58 @@ dsa_status dsa_prefill(const dsa_prefill_args* p, void* stream) {
   if (st == DSA_OK)
     st = check_attn(p->q, p->kv, (int)p->kv_dtype, p->kv_scale, p->attn_sink, p->topk_idxs, p->o,
                     p->batch, p->seq_q, p->seq_kv, p->heads, p->dqk, p->dv, p->topk);
-  if (st != DSA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return st;
+}
+
+dsa::TopkArgs prefill_topk_args(const dsa_prefill_args* p) {
+  return dsa::TopkArgs{p->logits, p->ks, p->ke, p->topk_idxs, p->batch, p->seq_q, p->seq_kv,
+                       p->topk};
+}
+
+dsa::AttnArgs prefill_attn_args(const dsa_prefill_args* p) {
+  return attn_args(p->q, p->kv, (int)p->kv_dtype, p->kv_scale, p->attn_sink, p->topk_idxs, p->o,
+                   p->batch, p->seq_q, p->seq_kv, p->heads, p->dqk, p->dv, p->topk, p->sm_scale);
+}
+
+// The top-k and the attention run one after the other on the stream, so
+// they share one workspace.
+size_t prefill_workspace_bytes(const dsa_prefill_args* p) {
+  const size_t a = dsa::topk_workspace_bytes(prefill_topk_args(p));
+  const size_t b = dsa::attn_workspace_bytes(prefill_attn_args(p));
+  return a > b ? a : b;
+}
+
+// The three stages on one stream with the given scratch.
+dsa_status run_prefill(const dsa_prefill_args* p, dsa::Workspace ws, hipStream_t s) {
   dsa::IndexerArgs ia{p->index_q, p->index_q_scale, p->index_k, p->index_k_scale,
                       p->index_weights, p->ks, p->ke, p->logits, p->batch, p->seq_q,
                       p->seq_kv, p->index_heads, p->index_dim};
-  st = finish(dsa::launch_indexer(ia, s), s);
+  dsa_status st = finish(dsa::launch_indexer(ia, s), s);
   if (st != DSA_OK) return st;
-  dsa::TopkArgs ta{p->logits, p->ks, p->ke, p->topk_idxs, p->batch, p->seq_q, p->seq_kv, p->topk};
-  st = finish(dsa::launch_topk(ta, s), s);
+  st = finish(dsa::launch_topk(prefill_topk_args(p), ws, s), s);
   if (st != DSA_OK) return st;
-  dsa::AttnArgs aa{p->q,     p->kv,     p->kv_dtype == DSA_KV_FP8_E4M3FN,
-                   p->kv_scale, p->attn_sink, p->topk_idxs,
-                   p->o,     p->batch,  p->seq_q,
-                   p->seq_kv, p->heads, p->dqk,
-                   p->dv,    p->topk,   p->sm_scale};
-  return finish(dsa::launch_attn(aa, s), s);
+  return finish(dsa::launch_attn(prefill_attn_args(p), ws, s), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_prefill_workspace_size(const dsa_prefill_args* p, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_VALUE;
+  const dsa_status st = check_prefill(p);
+  if (st != DSA_OK) return st;
+  *bytes = prefill_workspace_bytes(p);
+  return DSA_OK;
+}
+
+dsa_status dsa_prefill(const dsa_prefill_args* p, void* stream) {
+  dsa_status st = check_prefill(p);
+  if (st != DSA_OK) return st;
+  st = check_workspace(p->workspace, p->workspace_bytes, prefill_workspace_bytes(p));
+  if (st != DSA_OK) return st;
+  return run_prefill(p, dsa::Workspace{p->workspace, p->workspace_bytes},
+                     static_cast<hipStream_t>(stream));
 }
 
 const char* dsa_status_string(dsa_status s) {
@@ -144,6 +257,8 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_INVALID_VALUE: return "DSA_ERR_INVALID_VALUE: invalid argument";
     case DSA_ERR_NOT_SUPPORTED: return "DSA_ERR_NOT_SUPPORTED: no kernel for this shape";
     case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: kernel launch or execution failed";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace smaller than the call needs";
+    default: break;
   }
   return "unknown dsa_status";
 }

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace dsa {
@@ -42,26 +43,27 @@ struct AttnArgs {
   float sm_scale;
 };
 
+// Caller-provided device scratch (may be NULL / 0 bytes: the calls then take
+// their paths that need none).
+struct Workspace {
+  void* ptr;
+  size_t bytes;
+};
+
 bool indexer_supported(int H, int D);
 bool attn_supported(int Hq, int Dqk, int Dv, bool fp8);
 
-// Stream-ordered temporaries (hipMallocAsync) come from the current device's
-// default memory pool; keep freed blocks in the pool between calls.
-inline void keep_pool_memory() {
-  static bool done[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
-  hipMemPool_t pool;
-  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-    uint64_t thr = UINT64_MAX;
-    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
-  }
-  (void)hipGetLastError();
-  done[dev] = true;
-}
+// Compute units of the current device (cached per device, thread-safe).
+int device_cus();
+
+// Scratch bytes the fastest path of a call needs (0: none).  The launch
+// functions take that path only when the workspace holds at least as many
+// bytes, and a path without scratch otherwise.
+size_t topk_workspace_bytes(const TopkArgs& a);
+size_t attn_workspace_bytes(const AttnArgs& a);
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, Workspace ws, hipStream_t stream);
 
 }  // namespace dsa

@@ -455,13 +455,7 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   // least one key tile.
   // The persistent layout wants two items per workgroup, so that the snake
   // schedule can pair long windows with short ones.
-  int cus = 256;
-  {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
+  const int cus = device_cus();
   const long long slots = (long long)cus * (8 / kIdxWaves);  // 2 waves per SIMD, 4 SIMDs
   const long long tblocks = (long long)a.B * n_tblocks;
   const long long max_chunks = (a.N + kMinChunk - 1) / kMinChunk;

@@ -32,12 +32,13 @@
 //    K-major V layout addresses on its hardware.
 //  * Softmax in base 2 with sm_scale*log2(e) folded into one multiply, fp32
 //    state.  The reference of the exponent is fixed per head at the max of
-//    the first tile and never moved: o = O/l is exact for any reference,
-//    and p = 2^(s - ref) stays <= 2^16 as long as no later score exceeds the
-//    reference by more than 16 (log2 units).  If one does, the whole
-//    workgroup restarts the token with a max-only pre-pass and a second pass
-//    at the exact max.  The fp32 O accumulators are thus only ever touched
-//    by MFMA inside the loop (no per-tile rescale).
+//    the first tile and never moved: o = O/l is exact for any reference, and
+//    bf16 P and fp32 O and l carry p = 2^(s - ref) > 1 exactly as long as
+//    nothing overflows.  At the end of the token, a head whose per-lane sum
+//    of p passed 2^40 (so every p <= 2^40, far from the fp32 range) makes
+//    the whole workgroup restart the token with a max-only pre-pass and a
+//    second pass at the exact max.  The fp32 O accumulators are thus only
+//    ever touched by MFMA inside the loop (no per-tile rescale).
 //  * Tiles whose 32 indices are all invalid are skipped entirely.
 //  * FP8 KV (e4m3fn + per-row fp32 scale): the staged codes are widened to
 //    bf16 exactly (v_cvt_scalef32_pk_bf16_fp8) on the way into LDS; the row
@@ -775,27 +776,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const uint16_t* __restr
   *reinterpret_cast<uint2*>(o + ((size_t)row * Hq + h) * DV + cq) = pk2;
 }
 
-int device_cus() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-    return v;
-  return 256;
-}
-
-template <int DQK, int DV, bool FP8, int NW, int HPW>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  using C = AttnCfg<DQK, DV, FP8, NW, HPW>;
+// Splits of each row's K indices: with few rows (decode: B*M at most half
+// the compute units) each row is split over S workgroups, at least 4 tiles
+// each, so that the device is filled.  Returns S (1: unsplit) and the span.
+int attn_splits(const AttnArgs& a, int& kspan) {
   const long long rows = a.B * a.M;
-  if (rows > 0x7fffffffLL || a.K > kMaxK || a.Hq != NW * HPW) return hipErrorInvalidValue;
-  const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)DQK);
-  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  // Few rows (decode): split each row's K indices over S workgroups (at
-  // least 4 tiles each) so that the device is filled, and merge.  The
-  // partial results live in a stream-ordered workspace; without one the
-  // rows run unsplit.
   const int cus = device_cus();
-  int S = 1, kspan = a.K;
+  int S = 1;
+  kspan = a.K;
   if (rows * 2 <= cus) {
     const int want = (int)((cus + rows - 1) / rows);
     const int max_s = max(1, a.K / (4 * kBI));
@@ -804,42 +792,52 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     kspan = (kspan + kBI - 1) / kBI * kBI;
     S = (a.K + kspan - 1) / kspan;
   }
-  void* ws = nullptr;
-  if (S > 1) {
-    keep_pool_memory();
-    const size_t bytes = (size_t)rows * S * a.Hq * (DV * sizeof(uint16_t) + sizeof(float2));
-    if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) {
-      (void)hipGetLastError();
-      ws = nullptr;
-      S = 1;
-      kspan = a.K;
-    }
+  return S;
+}
+
+// Partial results of the splits: bf16 O_s / l_s [rows, S, Hq, Dv], then
+// fp32 (m_s, l_s) [rows, S, Hq].
+size_t attn_split_bytes(const AttnArgs& a, int S) {
+  if (S <= 1) return 0;
+  return (size_t)(a.B * a.M) * S * a.Hq * (a.Dv * sizeof(uint16_t) + sizeof(float2));
+}
+
+template <int DQK, int DV, bool FP8, int NW, int HPW>
+hipError_t launch(const AttnArgs& a, Workspace ws, hipStream_t stream) {
+  using C = AttnCfg<DQK, DV, FP8, NW, HPW>;
+  const long long rows = a.B * a.M;
+  if (rows > 0x7fffffffLL || a.K > kMaxK || a.Hq != NW * HPW) return hipErrorInvalidValue;
+  const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)DQK);
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // Few rows: split with a merge when the caller's workspace holds the
+  // partials; otherwise the rows run unsplit (same result).
+  int kspan;
+  int S = attn_splits(a, kspan);
+  const size_t need = attn_split_bytes(a, S);
+  if (S > 1 && (ws.ptr == nullptr || ws.bytes < need)) {
+    S = 1;
+    kspan = a.K;
   }
-  uint16_t* wso = static_cast<uint16_t*>(ws);
-  float2* wsml = ws ? reinterpret_cast<float2*>(wso + (size_t)rows * S * a.Hq * DV) : nullptr;
-  if (ws)
-    hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, true>),
-                       dim3((unsigned)(rows * S)), dim3(C::THREADS), 0, stream,
-                       (const uint16_t*)a.q, a.kv, a.kv_scale, a.attn_sink, a.topk_idxs,
-                       (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K, scale_log2, S, kspan, wso,
-                       wsml);
-  else
+  if (S == 1) {
     hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, false>), dim3((unsigned)rows),
                        dim3(C::THREADS), 0, stream, (const uint16_t*)a.q, a.kv, a.kv_scale,
                        a.attn_sink, a.topk_idxs, (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K,
                        scale_log2, 1, a.K, nullptr, nullptr);
-  hipError_t err = hipGetLastError();
-  if (ws) {
-    if (err == hipSuccess) {
-      constexpr int HPB = 256 / (DV / 4);
-      hipLaunchKernelGGL((attn_merge_kernel<DV>), dim3((unsigned)(rows * (a.Hq / HPB))), dim3(256),
-                         0, stream, wso, wsml, a.attn_sink, (uint16_t*)a.o, a.Hq, S);
-      err = hipGetLastError();
-    }
-    const hipError_t ferr = hipFreeAsync(ws, stream);
-    if (err == hipSuccess) err = ferr;
+    return hipGetLastError();
   }
-  return err;
+  uint16_t* wso = static_cast<uint16_t*>(ws.ptr);
+  float2* wsml = reinterpret_cast<float2*>(wso + (size_t)rows * S * a.Hq * DV);
+  hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, FP8, NW, HPW, true>),
+                     dim3((unsigned)(rows * S)), dim3(C::THREADS), 0, stream,
+                     (const uint16_t*)a.q, a.kv, a.kv_scale, a.attn_sink, a.topk_idxs,
+                     (uint16_t*)a.o, (int)a.M, (int)a.N, a.Hq, a.K, scale_log2, S, kspan, wso,
+                     wsml);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  constexpr int HPB = 256 / (DV / 4);
+  hipLaunchKernelGGL((attn_merge_kernel<DV>), dim3((unsigned)(rows * (a.Hq / HPB))), dim3(256), 0,
+                     stream, wso, wsml, a.attn_sink, (uint16_t*)a.o, a.Hq, S);
+  return hipGetLastError();
 }
 
 // Heads per wave at 128 heads (tuning knob: 32 -> 4 waves, 16 -> 8 waves).
@@ -848,12 +846,12 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
 #endif
 
 template <int DQK, int DV, bool FP8>
-hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_heads(const AttnArgs& a, Workspace ws, hipStream_t stream) {
   switch (a.Hq) {
-    case 16: return launch<DQK, DV, FP8, 1, 16>(a, stream);
-    case 32: return launch<DQK, DV, FP8, 2, 16>(a, stream);
-    case 64: return launch<DQK, DV, FP8, 4, 16>(a, stream);
-    case 128: return launch<DQK, DV, FP8, 128 / DSA_ATTN_HPW128, DSA_ATTN_HPW128>(a, stream);
+    case 16: return launch<DQK, DV, FP8, 1, 16>(a, ws, stream);
+    case 32: return launch<DQK, DV, FP8, 2, 16>(a, ws, stream);
+    case 64: return launch<DQK, DV, FP8, 4, 16>(a, ws, stream);
+    case 128: return launch<DQK, DV, FP8, 128 / DSA_ATTN_HPW128, DSA_ATTN_HPW128>(a, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -867,10 +865,15 @@ bool attn_supported(int Hq, int Dqk, int Dv, bool fp8) {
   return false;
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  if (a.Dqk == 64 && a.Dv == 64 && !a.fp8) return launch_heads<64, 64, false>(a, stream);
-  if (a.Dqk == 576 && a.Dv == 512 && !a.fp8) return launch_heads<576, 512, false>(a, stream);
-  if (a.Dqk == 576 && a.Dv == 512 && a.fp8) return launch_heads<576, 512, true>(a, stream);
+size_t attn_workspace_bytes(const AttnArgs& a) {
+  int kspan;
+  return attn_split_bytes(a, attn_splits(a, kspan));
+}
+
+hipError_t launch_attn(const AttnArgs& a, Workspace ws, hipStream_t stream) {
+  if (a.Dqk == 64 && a.Dv == 64 && !a.fp8) return launch_heads<64, 64, false>(a, ws, stream);
+  if (a.Dqk == 576 && a.Dv == 512 && !a.fp8) return launch_heads<576, 512, false>(a, ws, stream);
+  if (a.Dqk == 576 && a.Dv == 512 && a.fp8) return launch_heads<576, 512, true>(a, ws, stream);
   return hipErrorInvalidValue;
 }
 

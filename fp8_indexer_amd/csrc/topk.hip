@@ -72,18 +72,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int& total, int* sWave) {
   return pre + x - v;
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ logits,
-                                                          const int* __restrict__ ks,
-                                                          const int* __restrict__ ke,
-                                                          int* __restrict__ out, int N, int K,
-                                                          int skip_len) {
-  __shared__ uint32_t hist[4096];
-  __shared__ int sWave[kTkWaves];
-  __shared__ int sCnt[2][kTkWaves];
-  __shared__ int sSel[3];
-
+// One row (or, when skip_len > 0, only the rows longer than skip_len) per
+// iteration of a grid-stride loop: the launch can stay small when most rows
+// are left to the row kernel.
+__device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits,
+                                                const int* __restrict__ ks,
+                                                const int* __restrict__ ke,
+                                                int* __restrict__ out, int N, int K,
+                                                int skip_len, size_t r, uint32_t* hist,
+                                                int* sWave, int (*sCnt)[kTkWaves], int* sSel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t r = blockIdx.x;
   const int s = clampi(ks[r], 0, N);
   const int e = clampi(ke[r], s, N);
   const int len = e - s;
@@ -229,6 +227,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     eq_run += (int)__popcll(meq);
    }
   }
+  __syncthreads();  // LDS is reused by the next row
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ logits,
+                                                          const int* __restrict__ ks,
+                                                          const int* __restrict__ ke,
+                                                          int* __restrict__ out, int N, int K,
+                                                          int skip_len, int rows) {
+  __shared__ uint32_t hist[4096];
+  __shared__ int sWave[kTkWaves];
+  __shared__ int sCnt[2][kTkWaves];
+  __shared__ int sSel[3];
+  for (int r = blockIdx.x; r < rows; r += gridDim.x)
+    topk_stream_row(logits, ks, ke, out, N, K, skip_len, (size_t)r, hist, sWave, sCnt, sSel);
 }
 
 // ---- four waves per row ----------------------------------------------------
@@ -674,99 +686,110 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
   emit_selected<kSplitKR, false>(keys, n, tau, K - above, gt0, eq0, s0, nullptr, K, o, sCnt);
 }
 
-}  // namespace
+// Path of a call, chosen on the host from the sizes only (the windows are in
+// device memory): the bytes of scratch it needs.
+struct TopkPlan {
+  enum Path { kRows, kSplit, kTwoLevel } path;
+  int nseg;      // segments per row (split / two-level)
+  size_t bytes;  // scratch
+};
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+TopkPlan topk_plan(const TopkArgs& a) {
   const long long rows = a.B * a.M;
-  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-  // Rows of up to 8192 keys: kRowWaves waves per row, keys in VGPRs.  The
-  // path is chosen per row from its own window: with N > 8192 the row
-  // kernel still takes every row of up to 8192 keys, and the long-row
-  // kernels that follow skip those rows.
-  if (a.N <= kRowThreads * (4096 / kRowThreads)) {
-    hipLaunchKernelGGL(topk_row_kernel<4096 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
-                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
-    return hipGetLastError();
-  }
   // Few rows (decode) with windows that may pass 8192 keys: several
   // workgroups per row, every row (see the split kernels).
   const long long split_nseg = (a.N + kSplitKeys - 1) / kSplitKeys;
-  if (rows < 256 && a.N > kRowThreads * (8192 / kRowThreads) &&
-      rows * split_nseg * kRowThreads <= 0xffffffffLL) {
-    const int nseg = (int)split_nseg;
-    const size_t ws_bytes =
-        ((size_t)rows * kSplitRowWords + (size_t)rows * nseg * kSplitSegWords) * sizeof(uint32_t);
-    keep_pool_memory();
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_bytes, stream) == hipSuccess) {
-      uint32_t* w = static_cast<uint32_t*>(ws);
-      const dim3 grid((unsigned)(rows * nseg)), block(kRowThreads);
-      hipLaunchKernelGGL(topk_split_zero_kernel, dim3((unsigned)rows), block, 0, stream, w);
-      hipLaunchKernelGGL(topk_split_round_kernel<0>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         w, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_round_kernel<1>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         w, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_round_kernel<2>, grid, block, 0, stream, a.logits, a.ks, a.ke,
-                         w, (int)a.N, (int)a.K, nseg);
-      hipLaunchKernelGGL(topk_split_emit_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke, w,
-                         a.topk_idxs, (int)a.N, (int)a.K, nseg);
-      const hipError_t lerr = hipGetLastError();
-      const hipError_t ferr = hipFreeAsync(ws, stream);
-      return lerr != hipSuccess ? lerr : ferr;
-    }
-    (void)hipGetLastError();
-  }
+  if (a.N > kRowThreads * (8192 / kRowThreads) && rows < 256 &&
+      rows * split_nseg * kRowThreads <= 0xffffffffLL)
+    return {TopkPlan::kSplit, (int)split_nseg,
+            ((size_t)rows * kSplitRowWords + (size_t)rows * split_nseg * kSplitSegWords) *
+                sizeof(uint32_t)};
+  // Many rows, N > 8192: rows longer than 8192 keys in two levels through a
+  // candidate buffer (sized for every row: the host does not know which rows
+  // are long) while a row's candidates fit one workgroup's registers and the
+  // buffer stays at most 256 MiB; else one streaming workgroup per long row.
   const int nseg = (int)((a.N + kSegKeys - 1) / kSegKeys);
   const long long ncand = (long long)nseg * a.K;
-  const size_t ws_bytes = (size_t)rows * ncand * sizeof(int);
-  const bool two_level = a.N > kSegKeys && a.K <= kSegKeys && ncand <= kRowThreads * 64 &&
-                         rows * nseg <= 0x7fffffffLL && ws_bytes <= ((size_t)256 << 20);
-  // With few rows and two levels (the split kernels could not get their
-  // workspace), the two-level kernels take every row, as one more launch
-  // would cost more than the short rows gain.
+  const size_t cand_bytes = (size_t)rows * ncand * sizeof(int);
+  if (a.N > kSegKeys && a.K <= kSegKeys && ncand <= kRowThreads * 64 &&
+      rows * nseg <= 0x7fffffffLL && cand_bytes <= ((size_t)256 << 20))
+    return {TopkPlan::kTwoLevel, nseg, cand_bytes};
+  return {TopkPlan::kRows, nseg, 0};
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(const TopkArgs& a) { return topk_plan(a).bytes; }
+
+hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream) {
+  const long long rows = a.B * a.M;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  constexpr int kShort = kRowThreads * (8192 / kRowThreads);  // register-resident rows
+  // Rows of up to 4096 keys: kRowWaves waves per row, keys in VGPRs.
+  if (a.N <= kRowThreads * (4096 / kRowThreads)) {
+    hipLaunchKernelGGL(topk_row_kernel<4096 / kRowThreads>, dim3((unsigned)rows),
+                       dim3(kRowThreads), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N,
+                       (int)a.K);
+    return hipGetLastError();
+  }
+  TopkPlan plan = topk_plan(a);
+  if (plan.bytes > 0 && (ws.ptr == nullptr || ws.bytes < plan.bytes)) plan.path = TopkPlan::kRows;
+  if (plan.path == TopkPlan::kSplit) {
+    uint32_t* w = static_cast<uint32_t*>(ws.ptr);
+    const int nseg = plan.nseg;
+    const dim3 grid((unsigned)(rows * nseg)), block(kRowThreads);
+    hipLaunchKernelGGL(topk_split_zero_kernel, dim3((unsigned)rows), block, 0, stream, w);
+    hipLaunchKernelGGL(topk_split_round_kernel<0>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                       w, (int)a.N, (int)a.K, nseg);
+    hipLaunchKernelGGL(topk_split_round_kernel<1>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                       w, (int)a.N, (int)a.K, nseg);
+    hipLaunchKernelGGL(topk_split_round_kernel<2>, grid, block, 0, stream, a.logits, a.ks, a.ke,
+                       w, (int)a.N, (int)a.K, nseg);
+    hipLaunchKernelGGL(topk_split_emit_kernel, grid, block, 0, stream, a.logits, a.ks, a.ke, w,
+                       a.topk_idxs, (int)a.N, (int)a.K, nseg);
+    return hipGetLastError();
+  }
+  // With few rows and two levels, the two-level kernels take every row, as
+  // one more launch would cost more than the short rows gain.
+  const bool two_level = plan.path == TopkPlan::kTwoLevel;
   const bool rows_first = !(two_level && rows < 256);
-  const int skip_len = rows_first ? kRowThreads * (8192 / kRowThreads) : 0;
+  const int skip_len = rows_first ? kShort : 0;
   hipError_t err = hipSuccess;
   if (rows_first) {
-    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
-                       a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K);
+    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows),
+                       dim3(kRowThreads), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N,
+                       (int)a.K);
     err = hipGetLastError();
-    if (err != hipSuccess || a.N <= kRowThreads * (8192 / kRowThreads)) return err;
+    if (err != hipSuccess || a.N <= kShort) return err;
   }
-  // Longer rows: two levels through a stream-ordered candidate buffer while
-  // the candidates of a row fit one workgroup's registers and the buffer
-  // (sized for every row, since the host does not know which rows are long)
-  // stays modest; else one streaming workgroup per row.
   if (two_level) {
-    keep_pool_memory();
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_bytes, stream) == hipSuccess) {
-      int* cand = static_cast<int*>(ws);
-      hipLaunchKernelGGL(topk_seg_kernel, dim3((unsigned)(rows * nseg)), dim3(kRowThreads), 0,
-                         stream, a.logits, a.ks, a.ke, cand, (int)a.N, (int)a.K, nseg, skip_len);
-      err = hipGetLastError();
-      if (err == hipSuccess) {
-        if (ncand <= kRowThreads * 16)
-          hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)rows), dim3(kRowThreads), 0,
-                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg, skip_len);
-        else if (ncand <= kRowThreads * 32)
-          hipLaunchKernelGGL(topk_merge_kernel<32>, dim3((unsigned)rows), dim3(kRowThreads), 0,
-                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg, skip_len);
-        else
-          hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)rows), dim3(kRowThreads), 0,
-                             stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
-                             nseg, skip_len);
-        err = hipGetLastError();
-      }
-      const hipError_t ferr = hipFreeAsync(ws, stream);
-      return err != hipSuccess ? err : ferr;
-    }
-    (void)hipGetLastError();
+    int* cand = static_cast<int*>(ws.ptr);
+    const int nseg = plan.nseg;
+    const long long ncand = (long long)nseg * a.K;
+    hipLaunchKernelGGL(topk_seg_kernel, dim3((unsigned)(rows * nseg)), dim3(kRowThreads), 0,
+                       stream, a.logits, a.ks, a.ke, cand, (int)a.N, (int)a.K, nseg, skip_len);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (ncand <= kRowThreads * 16)
+      hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                         stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                         nseg, skip_len);
+    else if (ncand <= kRowThreads * 32)
+      hipLaunchKernelGGL(topk_merge_kernel<32>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                         stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                         nseg, skip_len);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)rows), dim3(kRowThreads), 0,
+                         stream, a.logits, a.ks, a.ke, cand, a.topk_idxs, (int)a.N, (int)a.K,
+                         nseg, skip_len);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a.logits,
-                     a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K, skip_len);
+  // Rows longer than 8192 keys (all rows when the row kernel did not run):
+  // one streaming workgroup per row, in a grid-stride loop over the rows so
+  // that a launch in which most rows are short stays small.
+  const long long sblocks = rows < 4LL * device_cus() ? rows : 4LL * device_cus();
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)sblocks), dim3(kTkThreads), 0, stream, a.logits,
+                     a.ks, a.ke, a.topk_idxs, (int)a.N, (int)a.K, skip_len, (int)rows);
   return hipGetLastError();
 }
 

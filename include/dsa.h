@@ -17,17 +17,27 @@
  *    environment variable DSA_SYNC_CHECK=1 is set, in which case the call
  *    waits for its kernels and reports their errors.
  *  * Ownership: the caller allocates and owns every buffer, including the
- *    intermediates of dsa_prefill.  The library keeps no pointer after a call
- *    returns.  The only device memory it takes are stream-ordered
- *    temporaries (hipMallocAsync / hipFreeAsync on the call's stream, from
- *    the device's default memory pool): dsa_topk's when N > 8192 and
- *    dsa_sparse_attn_fwd's for few query rows (also inside dsa_prefill),
- *    described there.  Calls are thread-safe.
+ *    intermediates of dsa_prefill and any device scratch ("workspace").  The
+ *    library allocates no device memory, keeps no pointer after a call
+ *    returns and holds no mutable global state other than a mutex-guarded
+ *    cache of each device's compute-unit count; calls are thread-safe.
+ *    Calls that can use scratch (dsa_topk, dsa_sparse_attn_fwd, dsa_prefill)
+ *    take a `workspace` pointer and its size in bytes; the matching
+ *    *_workspace_size call gives the bytes the fastest path needs for a
+ *    shape on the current device.  A NULL workspace (or a size of 0 bytes
+ *    needed) selects paths that need none, with the same results; a
+ *    non-NULL workspace smaller than the size query's answer gives
+ *    DSA_ERR_WORKSPACE.  The workspace must be 16-byte aligned.
+ *    The workspace is read and written by the enqueued kernels only, in
+ *    stream order: it must stay allocated until the stream has passed the
+ *    call, and two calls in flight at once need two workspaces.
  *  * Errors: arguments are checked on the host before anything is enqueued.
  *    NULL pointers, non-positive sizes, misalignment or inconsistent sizes
  *    give DSA_ERR_INVALID_VALUE; a valid shape with no compiled kernel gives
- *    DSA_ERR_NOT_SUPPORTED.  In both cases nothing is launched and no output
- *    is written.  A failed launch gives DSA_ERR_LAUNCH.
+ *    DSA_ERR_NOT_SUPPORTED; a too small workspace DSA_ERR_WORKSPACE.  In
+ *    these cases nothing is launched and no output is written.  A failed
+ *    launch gives DSA_ERR_LAUNCH.  The *_workspace_size calls validate
+ *    their sizes the same way and write *bytes only on DSA_OK.
  *  * Device-side data contracts are clamped or masked, never trapped: bounds
  *    are clamped, out-of-range indices are treated as -1.
  *  * FP8 means OCP float8 e4m3fn (1 sign, 4 exponent bits with bias 7, 3
@@ -38,24 +48,32 @@
 #ifndef DSA_H
 #define DSA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define DSA_VERSION 100 /* 1.0.0 */
+#define DSA_VERSION 200 /* 2.0.0: caller-owned workspace arguments */
 
 typedef enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_VALUE = 1,
   DSA_ERR_NOT_SUPPORTED = 2,
-  DSA_ERR_LAUNCH = 3
+  DSA_ERR_LAUNCH = 3,
+  DSA_ERR_WORKSPACE = 4, /* workspace given but smaller than the call needs */
+  DSA_STATUS_INT_ = 0x7fffffff /* not a status: makes every int value
+                                  representable (dsa_status_string accepts
+                                  any value) */
 } dsa_status;
 
 typedef enum dsa_kv_dtype {
   DSA_KV_BF16 = 0,       /* kv holds bf16 values                             */
-  DSA_KV_FP8_E4M3FN = 1  /* kv holds e4m3fn codes; value = code * kv_scale   */
+  DSA_KV_FP8_E4M3FN = 1, /* kv holds e4m3fn codes; value = code * kv_scale   */
+  DSA_KV_DTYPE_INT_ = 0x7fffffff /* not a dtype: makes every int value
+                                    representable, so that an invalid value
+                                    can be passed and rejected */
 } dsa_kv_dtype;
 
 /*
@@ -108,16 +126,20 @@ dsa_status dsa_indexer_logits(const void* q, const float* q_scale,
  *   ks, ke     [B, M]    int32
  *   topk_idxs  [B, M, K] int32 output
  * Supported: 1 <= K <= 4096, N < 2^31.  Output is deterministic.
- * Temporaries (N > 8192 only): with fewer than 256 rows, every row is cut
- * into 4096-key segments that share per-row digit histograms,
- * B*M*(6144 + ceil(N/4096)*1028)*4 bytes; with more rows, longer windows
- * go through a candidate buffer of B*M*ceil(N/8192)*K*4 bytes when that is
- * at most 256 MiB.  If an allocation fails (or the buffer would be larger),
- * a path without temporaries gives the same result.
+ * Workspace (dsa_topk_workspace_size; only N > 8192 needs any): with fewer
+ * than 256 rows every row is cut into 4096-key segments that share per-row
+ * digit histograms, B*M*(6144 + ceil(N/4096)*1028)*4 bytes; with more rows,
+ * windows longer than 8192 keys go through a candidate buffer of
+ * B*M*ceil(N/8192)*K*4 bytes when that is at most 256 MiB (0 bytes
+ * otherwise).  Without a workspace, rows longer than 8192 keys take one
+ * streaming workgroup each.
  */
+dsa_status dsa_topk_workspace_size(int64_t B, int64_t M, int64_t N, int32_t K, size_t* bytes);
+
 dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
                     int32_t* topk_idxs, int64_t B, int64_t M, int64_t N,
-                    int32_t K, void* stream);
+                    int32_t K, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /*
  * dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink.
@@ -143,20 +165,24 @@ dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
  *   sm_scale   softmax scale; <= 0 selects 1/sqrt(Dqk)
  * Supported: Hq in {16, 32, 64, 128}; (Dqk, Dv) in {(64, 64), (576, 512)}
  * (FP8 kv with (576, 512) only); 1 <= K <= 4096.
- * Few query rows (B*M at most half the device's compute units, as in
- * decode): each row's K indices are split over several workgroups whose
- * partial results are merged by a second kernel; the partials live in a
- * temporary taken with hipMallocAsync on `stream` from the device's default
- * memory pool (B*M*splits*Hq*(2*Dv + 8) bytes, splits <= K/128) and freed
- * with hipFreeAsync on the same stream.  If that allocation fails, the rows
- * run unsplit with the same result.
+ * Workspace (dsa_sparse_attn_workspace_size): with few query rows (B*M at
+ * most half the device's compute units, as in decode) each row's K indices
+ * are split over S workgroups whose partial results a second kernel merges;
+ * the partials take B*M*S*Hq*(2*Dv + 8) bytes (S <= K/128, chosen from the
+ * device's compute-unit count).  Without a workspace the rows run unsplit,
+ * with the same result up to rounding (the split stores its normalised
+ * partials in bf16).
  */
+dsa_status dsa_sparse_attn_workspace_size(int64_t B, int64_t M, int32_t Hq, int32_t Dqk,
+                                          int32_t Dv, int32_t K, size_t* bytes);
+
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
                                dsa_kv_dtype kv_dtype, const float* kv_scale,
                                const float* attn_sink,
                                const int32_t* topk_idxs, void* o, int64_t B,
                                int64_t M, int64_t N, int32_t Hq, int32_t Dqk,
                                int32_t Dv, int32_t K, float sm_scale,
+                               void* workspace, size_t workspace_bytes,
                                void* stream);
 
 /*
@@ -165,7 +191,9 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
  * meaning, layout and constraints of the same argument above; `logits` and
  * `topk_idxs` are caller-owned intermediates that hold the stage results when
  * the stream reaches the end of the call.  The argument struct is read during
- * the call only.
+ * the call only.  The stages run one after the other on `stream`, so one
+ * workspace serves both the top-k and the attention:
+ * dsa_prefill_workspace_size gives the larger of their needs.
  */
 typedef struct dsa_prefill_args {
   /* sizes */
@@ -198,8 +226,11 @@ typedef struct dsa_prefill_args {
   /* caller-owned intermediates */
   float* logits;              /* [B, M, N] */
   int32_t* topk_idxs;         /* [B, M, K] */
+  void* workspace;            /* device scratch or NULL */
+  size_t workspace_bytes;
 } dsa_prefill_args;
 
+dsa_status dsa_prefill_workspace_size(const dsa_prefill_args* args, size_t* bytes);
 dsa_status dsa_prefill(const dsa_prefill_args* args, void* stream);
 
 /* Static description of a status code (never NULL). */

@@ -45,6 +45,15 @@ def check_logits(gpu_rows, ref, terms, what=""):
     return float(d.max()) if d.size else 0.0
 
 
+def compare_topk(got, ref, what=""):
+    """Top-k rows must be bit-identical: got, ref [n, K] int32."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    bad = np.nonzero(~np.all(got == ref, axis=1))[0]
+    assert bad.size == 0, f"{what}: {bad.size} rows differ, first row {bad[0]}"
+
+
 def check_attn(o_gpu, o_ref, what=""):
     g = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"

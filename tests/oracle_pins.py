@@ -438,10 +438,63 @@ def check_attn_fp8_kv(seed=24):
     assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
 
 
+# ------------------------------------------------ row subsets (rows=...) --
+
+def check_rows_subsets(seed=31):
+    """The `rows=` path of each stage (the GPU tests compare sampled rows of
+    full-size workloads through it): every listed row, in the listed order,
+    must equal the independent reference for that row -- the brute-force sort
+    for top-k, exact rational scores for the indexer, the dense softmax for
+    attention -- with rows whose windows and index lists all differ, so a
+    wrong row mapping cannot pass."""
+    rng = np.random.default_rng(seed)
+    # top-k: distinct windows per row, rows listed out of order
+    M, N, K = 9, 60, 7
+    lg = rng.integers(-4, 5, (M, N)).astype(np.float32)
+    ks = np.int32([0, 3, 10, 20, 1, 33, 40, 0, 50])
+    ke = np.int32([60, 30, 18, 59, 9, 60, 47, 5, 58])
+    rows = np.int64([7, 2, 5, 0, 8])
+    got = oracle.topk(lg[rows], ks, ke, 1, M, N, K, rows=rows)
+    for i, r in enumerate(rows):
+        s, e = int(ks[r]), int(ke[r])
+        assert got[i].tolist() == _topk_ref(lg[r], s, e, K), ("topk rows", r)
+    # indexer: B = 2 so that rows of the second batch entry use its own keys
+    B, M2, N2, H, D = 2, 3, 7, 2, 4
+    q, qs, k, ksc, w, _, _ = _rand_indexer(rng, B=B, M=M2, N=N2, H=H, D=D)
+    ks2 = np.int32([[0, 2, 1], [3, 0, 5]])
+    ke2 = np.int32([[7, 5, 3], [7, 4, 7]])
+    rows2 = np.int64([4, 1, 5])
+    lg2 = oracle.indexer_logits(q, qs, k, ksc, w, ks2, ke2, rows=rows2)
+    qv = _torch_e4m3(q.ravel()).reshape(q.shape)
+    kv = _torch_e4m3(k.ravel()).reshape(k.shape)
+    for i, r in enumerate(rows2):
+        b, t = divmod(int(r), M2)
+        for key in range(N2):
+            inside = ks2[b, t] <= key < ke2[b, t]
+            assert np.isnan(lg2[i, key]) == (not inside), ("indexer window", r, key)
+            if inside:
+                acc = Fraction(0)
+                for h in range(H):
+                    dot = sum(Fraction(qv[b, t, h, d]) * Fraction(kv[b, key, d])
+                              for d in range(D))
+                    if dot > 0:
+                        acc += dot * Fraction(float(w[b, t, h])) * Fraction(float(qs[b, t, h]))
+                want = np.float32(float(acc * Fraction(float(ksc[b, key]))))
+                assert lg2[i, key] == want, ("indexer rows", r, key)
+    # attention: every row its own index list
+    qb, kvb, idx, sink = _rand_attn(rng, B=2, M=3, N=11, Hq=4, Dqk=8, K=6)
+    rows3 = np.int64([5, 0, 3])
+    got3 = oracle.sparse_attn(qb, kvb, sink, idx, 0.3, 8, rows=rows3)
+    qv3 = _torch_bf16(qb.view(np.uint16).ravel()).reshape(qb.shape)
+    kvv3 = _torch_bf16(kvb.view(np.uint16).ravel()).reshape(kvb.shape)
+    dense = _attn_dense(qv3, kvv3, sink, idx, 0.3, 8)
+    assert np.allclose(got3, dense[rows3], rtol=1e-12, atol=1e-12), "attention rows"
+
+
 ALL_CHECKS = [
     check_e4m3_decode, check_bf16_decode,
     check_indexer_hand, check_indexer_exact, check_indexer_invariants, check_indexer_terms,
     check_topk_hand, check_topk_bruteforce, check_topk_invariants,
     check_attn_hand, check_attn_dense, check_attn_closed_forms, check_attn_invariants,
-    check_attn_fp8_kv,
+    check_attn_fp8_kv, check_rows_subsets,
 ]

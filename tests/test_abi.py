@@ -28,8 +28,7 @@ def header_functions():
 
 def test_header_declares_the_four_stages():
     fns = header_functions()
-    for f in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_attn_fwd", "dsa_prefill",
-              "dsa_status_string", "dsa_version"):
+    for f in dsa.EXPORTS:
         assert f in fns
 
 
@@ -45,8 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = _lib()
-    assert dsa.version() == 100
-    for s in range(4):
+    assert dsa.version() == 200
+    for s in range(5):
         assert L.dsa_status_string(s)
     assert b"unknown" in L.dsa_status_string(99)
 
@@ -68,7 +67,7 @@ def test_prefill_struct_layout_matches_c(tmp_path):
         assert getattr(dsa.PrefillArgs, f).offset == off, f
 
 
-INVALID, UNSUPPORTED = 1, 2
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 4
 P = ctypes.c_void_p
 A16 = ctypes.c_void_p(0x10000)   # aligned fake pointers: never dereferenced,
 A4 = ctypes.c_void_p(0x20004)    # validation fails before any HIP call
@@ -101,19 +100,30 @@ def test_indexer_rejects_bad_arguments():
 def test_topk_rejects_bad_arguments():
     L = _lib()
     f = L.dsa_topk
-    assert f(None, A16, A16, A16, 1, 4, 8, 2, None) == INVALID
-    assert f(A16, A16, A16, A16, 1, 4, 8, 0, None) == INVALID
-    assert f(A16, A16, A16, A16, 0, 4, 8, 2, None) == INVALID
-    assert f(A16, A16, A16, A16, 1, 4, 8, 4097, None) == UNSUPPORTED
-    assert f(A16, A16, ctypes.c_void_p(0x10001), A16, 1, 4, 8, 2, None) == INVALID
+
+    def call(*a, ws=None, wsb=0):
+        return f(*a, ws, wsb, None)
+
+    assert call(None, A16, A16, A16, 1, 4, 8, 2) == INVALID
+    assert call(A16, A16, A16, A16, 1, 4, 8, 0) == INVALID
+    assert call(A16, A16, A16, A16, 0, 4, 8, 2) == INVALID
+    assert call(A16, A16, A16, A16, 1, 4, 8, 4097) == UNSUPPORTED
+    assert call(A16, A16, ctypes.c_void_p(0x10001), A16, 1, 4, 8, 2) == INVALID
+    # decode-shaped rows need scratch: a workspace one byte short is refused
+    need = dsa.topk_workspace_size(64, 1, 65536, 2048)
+    assert call(A16, A16, A16, A16, 64, 1, 65536, 2048, ws=A16, wsb=need - 1) == WORKSPACE
+    assert call(A16, A16, A16, A16, 64, 1, 65536, 2048, ws=ctypes.c_void_p(0x10008),
+                wsb=need) == INVALID  # workspace not 16-byte aligned
 
 
 def test_attention_rejects_bad_arguments():
     L = _lib()
     f = L.dsa_sparse_attn_fwd
 
-    def call(kv_dtype=0, kv_scale=None, Hq=128, Dqk=576, Dv=512, K=2048, q=A16, o=A16):
-        return f(q, A16, kv_dtype, kv_scale, None, A16, o, 1, 4, 8, Hq, Dqk, Dv, K, 0.0, None)
+    def call(kv_dtype=0, kv_scale=None, Hq=128, Dqk=576, Dv=512, K=2048, q=A16, o=A16, ws=None,
+             wsb=0, M=4):
+        return f(q, A16, kv_dtype, kv_scale, None, A16, o, 1, M, 8, Hq, Dqk, Dv, K, 0.0, ws, wsb,
+                 None)
 
     assert call(q=None) == INVALID
     assert call(kv_dtype=1) == INVALID                # fp8 kv needs kv_scale
@@ -126,6 +136,34 @@ def test_attention_rejects_bad_arguments():
     assert call(Dqk=128, Dv=128) == UNSUPPORTED
     assert call(K=5000) == UNSUPPORTED
     assert call(kv_dtype=1, kv_scale=A16, Dqk=64, Dv=64, Hq=16) == UNSUPPORTED
+    need = dsa.sparse_attn_workspace_size(1, 4, 128, 576, 512, 2048)
+    if need > 0:
+        assert call(ws=A16, wsb=need - 1) == WORKSPACE
+
+
+def test_workspace_size_queries():
+    """Sizes follow the documented formulas: none for short rows and many
+    query rows, per-row digit histograms for few long rows, candidates for
+    many long rows, and bf16 partials plus (m, l) for split attention rows;
+    invalid shapes are rejected like the calls themselves."""
+    assert dsa.topk_workspace_size(1, 4096, 4096, 2048) == 0
+    assert dsa.topk_workspace_size(1, 4096, 8192, 2048) == 0
+    # 64 rows, N = 65536: 16 segments of 4096 keys per row
+    assert dsa.topk_workspace_size(64, 1, 65536, 2048) == 64 * (6144 + 16 * 1028) * 4
+    # 300 rows of 20000 keys: 3 segments of 8192 keys, K candidates each
+    assert dsa.topk_workspace_size(1, 300, 20000, 100) == 300 * 3 * 100 * 4
+    # candidates beyond 256 MiB: none (streaming)
+    assert dsa.topk_workspace_size(1, 32768, 32768, 2048) == 0
+    # attention: many rows run unsplit; B*M <= CUs/2 rows are split
+    assert dsa.sparse_attn_workspace_size(1, 4096, 128, 576, 512, 2048) == 0
+    n = dsa.sparse_attn_workspace_size(64, 1, 128, 576, 512, 2048)
+    assert n > 0 and n % (64 * 128 * (2 * 512 + 8)) == 0
+    S = n // (64 * 128 * (2 * 512 + 8))
+    assert 2 <= S <= 2048 // 128
+    with pytest.raises(dsa.DSAError):
+        dsa.topk_workspace_size(1, 4, 8, 0)
+    with pytest.raises(dsa.DSAError):
+        dsa.sparse_attn_workspace_size(1, 4, 24, 576, 512, 2048)
 
 
 def test_prefill_rejects_null_and_inconsistent():

@@ -12,9 +12,9 @@ from gpu_util import check_attn, dev, log, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-def _run(x, idx, wl):
+def _run(x, idx, wl, workspace="auto"):
     o = dsa.sparse_attn_fwd(dev(x["q"]), dev(x["kv"]), dev(x["sink"]), dev(idx), wl.sm_scale,
-                            wl.Dv, kv_scale=dev(x["kv_scale"]))
+                            wl.Dv, kv_scale=dev(x["kv_scale"]), workspace=workspace)
     torch.cuda.synchronize()
     return o
 
@@ -112,17 +112,20 @@ def test_attn_workloads(name):
     log(f"  max|d| {mx:.3g} mean|d| {mn:.3g}")
 
 
+@pytest.mark.parametrize("workspace", ["auto", None], ids=["split", "unsplit"])
 @pytest.mark.parametrize("Hq", [128, 64])
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("where", ["middle", "last", "first", "moderate", "second_half"])
-def test_attn_reference_restart(fp8, where, Hq):
+def test_attn_reference_restart(fp8, where, Hq, workspace):
     """A score far above every score of the first tile (the kernel's fixed
     softmax reference: 72 natural units, p ~ 2^104) forces the max-only
     pre-pass and the second pass.  "moderate": ~21 natural units above (p ~
     2^30), which the fixed reference carries exactly without a restart.
-    "second_half": the big score in rows 16-31 of the first tile (with 64
-    heads the other key half's waves, whose maximum sets the shared
-    reference)."""
+    "second_half": the big score in rows 16-31 of the first tile (the second
+    16-row MFMA tile of the first gathered tile).  Two query rows: with a
+    workspace they run the split instance (each row's indices over several
+    workgroups), without one the unsplit instance that every prefill row
+    runs."""
     B, M, N, K = 1, 2, 600, 256
     wl = W.Workload("r", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
                     seed=6)
@@ -145,7 +148,8 @@ def test_attn_reference_restart(fp8, where, Hq):
     idx = np.tile(np.arange(0, 2 * K, 2, dtype=np.int32), (B, M, 1))  # rows 0,2,..,510
     idx[0, 0, K // 2] = big
     idx[0, 1, {"first": 0, "second_half": 20}.get(where, K - 1)] = big
-    o = _run(x, idx, wl)
+    log(f"attn restart {where} fp8={fp8} Hq={Hq} workspace={workspace}")
+    o = _run(x, idx, wl, workspace)
     ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
                              kv_scale=x["kv_scale"])
     check_attn(o, ref, f"restart/{where}")
@@ -171,3 +175,58 @@ def test_attn_split_rows_edge_cases(fp8, Hq):
     ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
                              kv_scale=x["kv_scale"])
     check_attn(o, ref, "split edge")
+
+
+@pytest.mark.parametrize("Hq,fp8", [(128, False), (64, True)])
+def test_attn_restart_many_rows(Hq, fp8):
+    """160 query rows (more than half the compute units: the unsplit
+    instance whatever the workspace) at the prefill head counts; every 7th
+    row holds one score ~72 natural units above its first tile's maximum
+    (a restart of that row's workgroup), at a varying position, the other
+    rows none."""
+    B, M, N, K = 1, 160, 3000, 512
+    wl = W.Workload("rm", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
+                    seed=12)
+    log(f"attn restart many rows Hq={Hq} fp8={fp8}")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(3)
+    qv = torch.ones((B, M, Hq, wl.Dqk), dtype=torch.float32) * 0.5
+    qv[..., ::2] = 1.0
+    x["q"] = qv.to(torch.bfloat16)
+    kvf = torch.from_numpy(rng.standard_normal((B, N, wl.Dqk)).astype(np.float32))
+    big = 2999
+    kvf[0, big] = 4.0
+    kvf[0, big, :8] = -3.0
+    if fp8:
+        x["kv"], x["kv_scale"] = W.quantize_e4m3fn_rows(kvf.numpy())
+    else:
+        x["kv"] = kvf.to(torch.bfloat16)
+    idx = np.stack([rng.choice(N - 1, size=K, replace=False) for _ in range(M)]).astype(np.int32)
+    idx = idx.reshape(B, M, K)
+    for t in range(0, M, 7):
+        idx[0, t, (37 * t) % K] = big
+    assert dsa.sparse_attn_workspace_size(B, M, Hq, 576, 512, K) == 0  # unsplit
+    o = _run(x, idx, wl)
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
+                             kv_scale=x["kv_scale"])
+    check_attn(o, ref, "restart many rows")
+
+
+@pytest.mark.parametrize("Hq,fp8", [(128, False), (64, True)])
+def test_attn_split_and_unsplit_agree(Hq, fp8):
+    """Decode-shaped rows (batch 8, K = 2048): the split instance (with a
+    workspace) and the unsplit one (without) both match the oracle."""
+    B, M, N, K = 8, 1, 6000, 2048
+    wl = W.Workload("su", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
+                    seed=13)
+    log(f"attn split/unsplit Hq={Hq} fp8={fp8}")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(8)
+    idx = np.stack([rng.choice(N, size=K, replace=False) for _ in range(B * M)]).astype(np.int32)
+    idx = idx.reshape(B, M, K)
+    idx[1, 0, 100:] = -1
+    assert dsa.sparse_attn_workspace_size(B, M, Hq, 576, 512, K) > 0
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
+                             kv_scale=x["kv_scale"])
+    check_attn(_run(x, idx, wl, "auto"), ref, "split")
+    check_attn(_run(x, idx, wl, None), ref, "unsplit")

@@ -6,21 +6,21 @@ import torch
 import fp8_indexer_amd as dsa
 import oracle
 import workloads as W
-from gpu_util import dev, log, sample_rows
+from gpu_util import compare_topk, dev, log, sample_rows
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(lg, ks, ke, K):
-    out = dsa.topk(dev(lg), dev(ks), dev(ke), K)
+def _run(lg, ks, ke, K, workspace="auto"):
+    out = dsa.topk(dev(lg), dev(ks), dev(ke), K, workspace=workspace)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _compare(lg, ks, ke, K, rows=None, what=""):
+def _compare(lg, ks, ke, K, rows=None, what="", workspace="auto"):
     lg = np.ascontiguousarray(lg, np.float32)
     B, M, N = lg.shape
-    g = _run(lg, ks, ke, K).reshape(B * M, K)
+    g = _run(lg, ks, ke, K, workspace).reshape(B * M, K)
     flat = lg.reshape(B * M, N)
     if rows is None:
         ref = oracle.topk(flat, ks, ke, B, M, N, K)
@@ -28,8 +28,7 @@ def _compare(lg, ks, ke, K, rows=None, what=""):
     else:
         ref = oracle.topk(flat[rows], ks, ke, B, M, N, K, rows=rows)
         got = g[rows]
-    bad = np.nonzero(~np.all(got == ref, axis=1))[0]
-    assert bad.size == 0, f"{what}: {bad.size} rows differ, first row {bad[0]}"
+    compare_topk(got, ref, what)
 
 
 def _dist(kind, shape, rng):
@@ -68,16 +67,20 @@ def test_topk_small(kind, K):
     _compare(lg, ks, ke, K, what=f"{kind}/K{K}")
 
 
-def test_topk_long_rows_streaming():
-    """Rows longer than the register-resident limit (8192 keys)."""
+@pytest.mark.parametrize("workspace", ["auto", None], ids=["split", "streaming"])
+def test_topk_long_rows(workspace):
+    """Rows longer than the register-resident limit (8192 keys), few rows:
+    with a workspace the rows are split into segments sharing digit
+    histograms; without one each long row takes one streaming workgroup."""
     rng = np.random.default_rng(11)
     B, M, N, K = 2, 3, 70000, 2048
     lg = _dist("special", (B, M, N), rng)
     ks = np.array([[0, 100, 60000], [0, 5, 0]], np.int32)
     ke = np.array([[70000, 8300, 70000], [65536, 8197, 2048]], np.int32)
-    _compare(lg, ks, ke, K, what="long rows")
+    log(f"topk long rows workspace={workspace}")
+    _compare(lg, ks, ke, K, what="long rows", workspace=workspace)
     lg2 = _dist("ties", (B, M, N), rng)
-    _compare(lg2, ks, ke, 4096, what="long rows K=4096 ties")
+    _compare(lg2, ks, ke, 4096, what="long rows K=4096 ties", workspace=workspace)
 
 
 def test_topk_deterministic():
@@ -126,8 +129,9 @@ def test_topk_split_rows(kind, K):
     _compare(lg, ks, ke, K, what=f"split rows {kind}/K{K}")
 
 
+@pytest.mark.parametrize("workspace", ["auto", None], ids=["two_level", "streaming"])
 @pytest.mark.parametrize("K", [100, 2048])
-def test_topk_two_level_many_rows(K):
+def test_topk_two_level_many_rows(K, workspace):
     """At least 256 rows with N > 8192: rows of up to 8192 keys go to the
     register-resident kernel; longer ones are cut into 8192-key segments
     whose top-K candidates are then reduced."""
@@ -138,8 +142,8 @@ def test_topk_two_level_many_rows(K):
     ke = (ks + rng.integers(0, N - 3000, (B, M))).astype(np.int32)
     ks[0, :6] = [0, 0, 0, 5, 0, 19000]
     ke[0, :6] = [N, 8192, 8193, 16390, K, N]
-    log(f"topk two-level many rows K={K}")
-    _compare(lg, ks, ke, K, what=f"two-level many rows K{K}")
+    log(f"topk two-level many rows K={K} workspace={workspace}")
+    _compare(lg, ks, ke, K, what=f"two-level many rows K{K}", workspace=workspace)
 
 
 def test_topk_many_long_rows_streaming():
@@ -165,5 +169,4 @@ def test_topk_many_long_rows_streaming():
                                      long_rows]))
     flat = lg.numpy().reshape(M, N)
     ref = oracle.topk(flat[rows], ks, ke, B, M, N, K, rows=rows)
-    bad = np.nonzero(~np.all(g[rows] == ref, axis=1))[0]
-    assert bad.size == 0, f"{bad.size} rows differ, first row {rows[bad[0]]}"
+    compare_topk(g[rows], ref, "many long rows")

@@ -38,6 +38,13 @@ MUTANTS = [
     ("minus_one_not_masked", "if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];",
      "if (idx[j] < N) J[nj++] = idx[j] < 0 ? 0 : idx[j];"),
     ("fp8_kv_scale_ignored", "(double)kv_scale[b * N + J[j]];", "1.0;"),
+    # row-subset paths: the listed row's own window / query / index list
+    ("topk_rows_window", "window(ks, ke, r, N, &s, &e);\n      int32_t* o = out + i * K;",
+     "window(ks, ke, i, N, &s, &e);\n      int32_t* o = out + i * K;"),
+    ("indexer_rows_query", "const uint8_t* qr = q + (r * H + h) * D;",
+     "const uint8_t* qr = q + (i * H + h) * D;"),
+    ("attn_rows_indices", "const int32_t* idx = topk_idxs + r * K;",
+     "const int32_t* idx = topk_idxs + i * K;"),
 ]
 
 
@@ -54,9 +61,11 @@ def test_pins_catch_mutant(mutant_dir, name, orig, mut):
         '#include "dsa_oracle.h"', f'#include "{os.path.join(os.path.dirname(obuild.SRC), "dsa_oracle.h")}"'))
     lib = str(mutant_dir / f"lib{name}.so")
     obuild.build(out=lib, src=str(src), extra_flags=("-w",))
-    # A mutant may write out of bounds: run it in a forked child so it cannot
-    # corrupt this process.  A crash also counts as caught.
-    ctx = mp.get_context("fork")
+    # A mutant may write out of bounds: run it in a child process so it cannot
+    # corrupt this process.  A crash also counts as caught.  The child is
+    # spawned, not forked: a fork after this process has run OpenMP regions
+    # (any earlier oracle call) would leave the child's thread pool unusable.
+    ctx = mp.get_context("spawn")
     rd, wr = ctx.Pipe(duplex=False)
     proc = ctx.Process(target=_run_checks, args=(lib, wr))
     proc.start()
