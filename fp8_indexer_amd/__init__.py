@@ -26,13 +26,15 @@ import torch
 
 __all__ = ["DSAError", "lib", "version", "indexer_logits", "topk", "sparse_attn_fwd",
            "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
-           "prefill_workspace_size", "KV_BF16", "KV_FP8_E4M3FN", "LIB_PATH"]
+           "prefill_workspace_size", "prefill_noalloc", "KV_BF16", "KV_FP8_E4M3FN",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 KV_BF16, KV_FP8_E4M3FN = 0, 1
 EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_workspace_size", "dsa_prefill", "dsa_prefill_workspace_size",
-           "dsa_status_string", "dsa_version")
+           "dsa_prefill_noalloc", "dsa_status_string", "dsa_version")
+NOALLOC_SCRATCH_BYTES = 48 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 
 
 class DSAError(RuntimeError):
@@ -86,6 +88,8 @@ def lib():
         L.dsa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs), psz]
         L.dsa_prefill.restype = ctypes.c_int
         L.dsa_prefill.argtypes = [ctypes.POINTER(PrefillArgs), P]
+        L.dsa_prefill_noalloc.restype = ctypes.c_int
+        L.dsa_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), P]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_version.restype = ctypes.c_int
@@ -312,4 +316,19 @@ def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, k
         wp, wn, _keep = _workspace(workspace, need, q.device)
         a.workspace, a.workspace_bytes = (wp.value if wp is not None else None), wn
         _check("dsa_prefill", lib().dsa_prefill(ctypes.byref(a), _stream(q)))
+    return logits, topk_idxs, out
+
+
+def prefill_noalloc(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q,
+                    kv, attn_sink, sm_scale=0.0, dv=None, kv_scale=None, logits=None,
+                    topk_idxs=None, out=None):
+    """dsa_prefill_noalloc: the whole path with the library's static device
+    scratch instead of a workspace (no device allocation by the library;
+    outputs not passed in are still allocated here).  Calls on one device
+    must not overlap."""
+    a, logits, topk_idxs, out = _prefill_args(
+        index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
+        attn_sink, sm_scale, dv, kv_scale, logits, topk_idxs, out)
+    with torch.cuda.device(q.device):
+        _check("dsa_prefill_noalloc", lib().dsa_prefill_noalloc(ctypes.byref(a), _stream(q)))
     return logits, topk_idxs, out

@@ -251,6 +251,57 @@ dsa_status dsa_prefill(const dsa_prefill_args* p, void* stream) {
                      static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of dsa_prefill_noalloc: one copy per device, for the life of the
+// process.  In host code `scratch` only names the symbol; the device address
+// of each device's copy comes from hipGetSymbolAddress with that device
+// current, and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch (looked up once per device), or
+// nullptr if the lookup failed.
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_prefill_noalloc(const dsa_prefill_args* p, void* stream) {
+  dsa_status st = check_prefill(p);
+  if (st != DSA_OK) return st;
+  if (p->workspace != nullptr || p->workspace_bytes != 0) return DSA_ERR_INVALID_VALUE;
+  const size_t need = prefill_workspace_bytes(p);
+  if (need > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return DSA_ERR_LAUNCH;
+    }
+    ws = scratch_address(dev);
+    if (ws == nullptr) return DSA_ERR_LAUNCH;
+  }
+  return run_prefill(p, dsa::Workspace{ws, need}, static_cast<hipStream_t>(stream));
+}
+
 const char* dsa_status_string(dsa_status s) {
   switch (s) {
     case DSA_OK: return "DSA_OK";

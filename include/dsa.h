@@ -233,6 +233,28 @@ typedef struct dsa_prefill_args {
 dsa_status dsa_prefill_workspace_size(const dsa_prefill_args* args, size_t* bytes);
 dsa_status dsa_prefill(const dsa_prefill_args* args, void* stream);
 
+/*
+ * dsa_prefill_noalloc -- dsa_prefill for callers that cannot allocate device
+ * memory at all: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  It computes exactly what dsa_prefill
+ * computes with a workspace of dsa_prefill_workspace_size bytes, taking that
+ * scratch from a static device array of DSA_NOALLOC_SCRATCH_BYTES inside the
+ * library (one copy per device, held from the library's load until the
+ * process ends) instead of a caller workspace.  `args->workspace` must be
+ * NULL and `args->workspace_bytes` 0.
+ *  * A shape whose scratch need exceeds DSA_NOALLOC_SCRATCH_BYTES is
+ *    rejected with DSA_ERR_WORKSPACE before anything is enqueued (e.g. the
+ *    top-k of fewer than 256 rows of more than ~3M keys).
+ *  * The array is shared by every call on a device and keeps the last
+ *    call's contents (the kernels clear what they need cleared themselves):
+ *    calls that overlap on one device -- two streams, or two host threads --
+ *    race on it and must be serialised by the caller.
+ *  * The first call on a device looks up that device's copy of the array
+ *    (no allocation); calls are otherwise like dsa_prefill.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+dsa_status dsa_prefill_noalloc(const dsa_prefill_args* args, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* dsa_status_string(dsa_status s);
 

@@ -178,3 +178,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dsa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         dsa.lib()
+
+
+def test_prefill_noalloc_rejects_before_launch():
+    """The static-scratch entry point refuses a workspace argument and a
+    shape whose scratch need exceeds its static array, before any HIP call."""
+    L = _lib()
+    a = dsa.PrefillArgs(batch=100, seq_q=1, seq_kv=1 << 24, index_q=0x10000,
+                        index_k=0x10000, index_k_scale=0x10000, index_weights=0x10000,
+                        ks=0x10000, ke=0x10000, index_heads=64, index_dim=128, topk=2048,
+                        q=0x10000, kv=0x10000, kv_dtype=0, o=0x10000, heads=128, dqk=576,
+                        dv=512, logits=0x10000, topk_idxs=0x10000)
+    assert dsa.prefill_workspace_size(a) > dsa.NOALLOC_SCRATCH_BYTES
+    assert L.dsa_prefill_noalloc(ctypes.byref(a), None) == WORKSPACE
+    a.workspace, a.workspace_bytes = 0x10000, 1 << 30
+    assert L.dsa_prefill_noalloc(ctypes.byref(a), None) == INVALID
+    assert L.dsa_prefill_noalloc(None, None) == INVALID
