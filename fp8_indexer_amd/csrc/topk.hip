@@ -43,21 +43,85 @@ constexpr int kEPT = 16;  // register-resident keys per lane
 // Order-preserving key: larger float -> larger unsigned key.  NaN -> key of
 // -inf; -0 -> key of +0.
 __device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) b = 0xFF800000u;  // NaN -> -inf
-  if (b == 0x80000000u) b = 0u;                           // -0 -> +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const float z = v + 0.0f;  // -0 -> +0 (IEEE sum of opposite zeros); NaN stays NaN
+  const uint32_t b = __builtin_isnan(z) ? 0xFF800000u : __float_as_uint(z);  // NaN -> -inf
+  // negative: all bits flipped; positive: sign bit set
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+// Row elements first + 64 c (c < KR) of a row of n floats into v[c], with
+// 0.0 for positions >= n: buffer loads, whose range check against n does
+// the bounds test (nothing is read past the row) with no per-lane address
+// arithmetic; slots are grouped by 16 so that every slot's offset inside
+// its group fits the instruction's immediate field.
+template <int KR>
+__device__ __forceinline__ void load_row(const float* __restrict__ row, int n, int first,
+                                         float (&v)[KR]) {
+#pragma unroll
+  for (int g = 0; g < KR; g += 16) {
+    const int rem = n - g * kWave;  // elements of the row from this group on
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row) + g * kWave, (short)0, rem > 0 ? rem * 4 : 0, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 16 && g + j < KR; ++j)
+      v[g + j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, first * 4 + j * kWave * 4, 0, 0));
+  }
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value, so that per-wave loop bounds and offsets stay scalar.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Number of lanes below the calling lane whose bit is set in mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Key of element min(i, n - 1) of a row of n >= 1 floats.  Positions i >= n
+// get a real key of the row: every user masks them by position.  The load is
+// unconditional and always in bounds, so that a loop of these issues every
+// load before waiting on the first (a load under a per-lane branch is waited
+// for before the next one is issued).
+__device__ __forceinline__ uint32_t key_clamped(const float* __restrict__ row, int i, int n) {
+  return order_key(row[i < n ? i : n - 1]);
+}
+
+// Keys at positions >= n (loaded from a clamped position) become 0, which
+// is below the key of every float (the smallest, -inf's, is 0x007FFFFF), so
+// they are never selected, never equal the threshold, and fall into digit
+// bin 0 of the first round, which no real key reaches: the counting and
+// emission loops need no per-lane position test.  Position of keys[c]:
+// first + 64 c.  The empty asm makes every load complete before the first
+// test, so that the compiler cannot move the loads back under it.
+template <int KR>
+__device__ __forceinline__ void mask_tail(uint32_t (&keys)[KR], int first, int n) {
+#pragma unroll
+  for (int c = 0; c < KR; ++c) asm volatile("" : "+v"(keys[c]));
+#pragma unroll
+  for (int c = 0; c < KR; ++c) keys[c] = first + c * kWave < n ? keys[c] : 0u;
+}
+
+// Inclusive prefix sum over the 64 lanes (lane order) with DPP: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16 (lanes with no source add 0),
+// then the last lane of each row is broadcast into the rows above it.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
 }
 
 // Exclusive prefix sum over the 512 threads of the block (thread order).
 __device__ __forceinline__ int block_excl_scan(int v, int& total, int* sWave) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int x = wave_incl_scan(v);
   if (lane == 63) sWave[wave] = x;
   __syncthreads();
   int pre = 0, tot = 0;
@@ -81,7 +145,7 @@ __device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits
                                                 int* __restrict__ out, int N, int K,
                                                 int skip_len, size_t r, uint32_t* hist,
                                                 int* sWave, int (*sCnt)[kTkWaves], int* sSel) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int s = clampi(ks[r], 0, N);
   const int e = clampi(ke[r], s, N);
   const int len = e - s;
@@ -101,7 +165,7 @@ __device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits
 #pragma unroll
     for (int c = 0; c < kEPT; ++c) {
       const int i = s + c * kTkThreads + tid;
-      keys[c] = (c < nch && i < e) ? order_key(row[i]) : 0u;
+      keys[c] = key_clamped(row, c < nch ? i : e - 1, e);
     }
   }
   auto get = [&](int c) -> uint32_t {
@@ -112,7 +176,7 @@ __device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits
       return v;
     }
     const int i = s + c * kTkThreads + tid;
-    return i < e ? order_key(row[i]) : 0u;
+    return key_clamped(row, i, e);
   };
 
   // ---- three MSD rounds: 12 + 10 + 10 key bits ---------------------------
@@ -177,7 +241,7 @@ __device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits
   // exchanges the counts, then it writes its segment with ballots.
   const int segw = (len + kTkWaves * kWave - 1) / (kTkWaves * kWave) * kWave;
   const int wb = wave * segw;
-  auto key_at = [&](int i) -> uint32_t { return i < len ? order_key(row[s + i]) : 0u; };
+  auto key_at = [&](int i) -> uint32_t { return key_clamped(row + s, i, len); };
   int gtc = 0, eqc = 0;
 #pragma unroll 1
   for (int c0 = 0; c0 < segw; c0 += 8 * kWave) {
@@ -203,29 +267,26 @@ __device__ __forceinline__ void topk_stream_row(const float* __restrict__ logits
     gt_base += w < wave ? sCnt[0][w] : 0;
     eq_base += w < wave ? sCnt[1][w] : 0;
   }
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_run = eq_base, sel_run = gt_base + min(eq_base, n_eq);
 #pragma unroll 1
   for (int c0 = 0; c0 < segw; c0 += 8 * kWave) {
-   uint32_t uu[8];
+    uint32_t uu[8];
 #pragma unroll
-   for (int j = 0; j < 8; ++j) uu[j] = key_at(wb + c0 + j * kWave + lane);
+    for (int j = 0; j < 8; ++j) uu[j] = key_at(wb + c0 + j * kWave + lane);
 #pragma unroll
-   for (int j = 0; j < 8; ++j) {
-    const int i = wb + c0 + j * kWave + lane;
-    const bool in = c0 + j * kWave < segw && i < len;
-    const uint32_t u = uu[j];
-    const bool gt = in && u > tau;
-    const bool eq = in && u == tau;
-    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
-    const int eq_before = (int)__popcll(meq & lt_mask);
-    const int eq_left = max(0, n_eq - eq_run);
-    const bool eq_sel = eq && eq_before < eq_left;
-    const int pos = sel_run + (int)__popcll(mgt & lt_mask) + min(eq_before, eq_left);
-    if ((gt || eq_sel) && pos < K) o[pos] = s + i;
-    sel_run += (int)__popcll(mgt) + min((int)__popcll(meq), eq_left);
-    eq_run += (int)__popcll(meq);
-   }
+    for (int j = 0; j < 8; ++j) {
+      const int i = wb + c0 + j * kWave + lane;
+      const bool in = c0 + j * kWave < segw && i < len;
+      const uint32_t u = uu[j];
+      const bool eq = in && u == tau;
+      const uint64_t meq = __ballot(eq);
+      const bool sel = (in && u > tau) || (eq && eq_run + lanes_below(meq) < n_eq);
+      const uint64_t msel = __ballot(sel);
+      const int pos = sel_run + lanes_below(msel);
+      if (sel && pos < K) o[pos] = s + i;
+      sel_run += (int)__popcll(msel);
+      eq_run += (int)__popcll(meq);
+    }
   }
   __syncthreads();  // LDS is reused by the next row
 }
@@ -256,16 +317,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 constexpr int kRowWaves = DSA_TOPK_ROW_WAVES;  // waves per row (tuning knob)
 constexpr int kRowThreads = kRowWaves * kWave;
 
-// Inclusive prefix sum over the 64 lanes (lane order).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
 
 // One MSD round's threshold: hist[0..nb) counts the remaining keys by digit
 // (larger digit = larger key); returns the digit bin holding the krem-th
@@ -274,7 +325,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // hist may be in LDS or in global memory; sSel holds 3 ints.
 __device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
                                               int* sSel) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int bpt = nb / kRowThreads;  // bins per thread
   int tsum = 0;
   for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
@@ -311,7 +362,7 @@ __host__ __device__ constexpr int digit_shift(int round) {
 }
 
 // Emission of a workgroup's keys (wave w holds positions w*64*KR + c*64 +
-// lane, len of them): every key > tau and the first n_eq keys == tau of the
+// lane, len of them; keys at positions >= len are 0, see mask_tail): every key > tau and the first n_eq keys == tau of the
 // whole row go to o in ascending position order.  gt0 / eq0: keys > tau /
 // == tau at positions before this workgroup's (other workgroups of the same
 // row).  Writes o[pos] = first + i, or cand[i] when GATHER.
@@ -321,15 +372,14 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int le
                                               const int* __restrict__ cand, int K,
                                               int* __restrict__ o, int (*sCnt)[kRowWaves]) {
   constexpr int SEG = kWave * KR;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int base = wave * SEG;
   int gtc = 0, eqc = 0;
 #pragma unroll
   for (int c = 0; c < KR; ++c) {
     if (base + c * kWave >= len) break;
-    const int i = base + c * kWave + lane;
-    gtc += (int)__popcll(__ballot(i < len && keys[c] > tau));
-    eqc += (int)__popcll(__ballot(i < len && keys[c] == tau));
+    gtc += (int)__popcll(__builtin_amdgcn_ballot_w64(keys[c] > tau));
+    eqc += (int)__popcll(__builtin_amdgcn_ballot_w64(keys[c] == tau));
   }
   if (lane == 0) {
     sCnt[0][wave] = gtc;
@@ -342,24 +392,32 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int le
     gt_base += w < wave ? sCnt[0][w] : 0;
     eq_base += w < wave ? sCnt[1][w] : 0;
   }
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // a key is selected if it is above tau, or equal to tau and among the
+  // first n_eq such keys of the row; its slot is the number of selected
+  // keys before it
+  // The output goes through a buffer resource of K entries: its range check
+  // drops any store past o[K - 1].  Keys equal to tau are rare (with
+  // distinct values, one per row), so their test runs only in slots that
+  // hold one.
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(o, (short)0, K * 4, 0x00020000);
   int eq_run = eq_base, sel_run = gt_base + min(eq_base, n_eq);
 #pragma unroll
   for (int c = 0; c < KR; ++c) {
     if (base + c * kWave >= len) break;
     const int i = base + c * kWave + lane;
     const uint32_t u = keys[c];
-    const bool valid = i < len;
-    const bool gt = valid && u > tau;
-    const bool eq = valid && u == tau;
-    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
-    const int eq_before = __popcll(meq & lt_mask);
-    const int eq_left = max(0, n_eq - eq_run);
-    const bool eq_sel = eq && eq_before < eq_left;
-    const int pos = sel_run + __popcll(mgt & lt_mask) + min(eq_before, eq_left);
-    if ((gt || eq_sel) && pos < K) o[pos] = GATHER ? cand[i] : first + i;
-    sel_run += __popcll(mgt) + min((int)__popcll(meq), eq_left);
-    eq_run += __popcll(meq);
+    const bool eq = u == tau;
+    const uint64_t meq = __builtin_amdgcn_ballot_w64(eq);
+    bool sel = u > tau;
+    if (meq != 0ull) sel = sel | (eq & (lanes_below(meq) + eq_run < n_eq));
+    const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
+    if (sel) {
+      const int pos = lanes_below(msel) + sel_run;
+      __builtin_amdgcn_raw_buffer_store_b32(GATHER ? cand[i] : first + i, ro, pos * 4, 0, 0);
+    }
+    sel_run += (int)__popcll(msel);
+    eq_run += (int)__popcll(meq);
   }
 }
 
@@ -373,14 +431,25 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
                                            int K, int* __restrict__ o, uint32_t* hist, int* sRed,
                                            int* sSel, int (*sCnt)[kRowWaves]) {
   constexpr int SEG = kWave * KR;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int base = wave * SEG;
   uint32_t keys[KR];
+  if constexpr (GATHER) {
 #pragma unroll
-  for (int c = 0; c < KR; ++c) {
-    const int i = base + c * kWave + lane;
-    keys[c] = i < len ? order_key(GATHER ? src[cand[i]] : src[i]) : 0u;
+    for (int c = 0; c < KR; ++c) {
+      const int i = base + c * kWave + lane;
+      keys[c] = (uint32_t)cand[i < len ? i : len - 1];  // candidate positions first
+    }
+#pragma unroll
+    for (int c = 0; c < KR; ++c)
+      keys[c] = order_key(src[(int)keys[c]]);  // an in-row position for every lane
+  } else {
+    float v[KR];
+    load_row<KR>(src, len, base + lane, v);
+#pragma unroll
+    for (int c = 0; c < KR; ++c) keys[c] = order_key(v[c]);
   }
+  mask_tail<KR>(keys, base + lane, len);
 
   // After a round whose threshold bin holds exactly the keys still needed,
   // every key of that bin is selected, so the keys >= its smallest key (the
@@ -401,9 +470,8 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 #pragma unroll
       for (int c = 0; c < KR; ++c) {
         if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
-        const int i = base + c * kWave + lane;
         const uint32_t u = keys[c];
-        if (i < len && (round == 0 || (u >> (shift + bits)) == prefix))
+        if (round == 0 || (u >> (shift + bits)) == prefix)
           atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
@@ -553,12 +621,12 @@ __device__ __forceinline__ int split_load(const float* __restrict__ logits,
   const int n = min(e - s0, kSplitKeys);
   if (n <= 0) return 0;
   const float* src = logits + r * (size_t)N + s0;
-  const int base = (threadIdx.x >> 6) * (kWave * kSplitKR) + (threadIdx.x & 63);
+  const int base = wave_id() * (kWave * kSplitKR) + (threadIdx.x & 63);
+  float v[kSplitKR];
+  load_row<kSplitKR>(src, n, base, v);
 #pragma unroll
-  for (int c = 0; c < kSplitKR; ++c) {
-    const int i = base + c * kWave;
-    keys[c] = i < n ? order_key(src[i]) : 0u;
-  }
+  for (int c = 0; c < kSplitKR; ++c) keys[c] = order_key(v[c]);
+  mask_tail<kSplitKR>(keys, base, n);
   return n;
 }
 
@@ -585,7 +653,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_round_kernel(
   __shared__ int sRed[kRowWaves];
   __shared__ int sSel[3];
   constexpr int bits = digit_bits(ROUND), shift = digit_shift(ROUND), nb = 1 << bits;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   size_t r;
   int s0;
   uint32_t keys[kSplitKR];
