@@ -429,18 +429,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     const int id = blockIdx.x % per_batch;
     process(blockIdx.x / per_batch, n_tblocks - 1 - id / n_chunks, id % n_chunks);
   } else {
-    // Persistent: items are numbered chunk-major, latest token blocks first
-    // (descending work for causal-like windows), and workgroup g takes items
-    // g, 2G-1-g, 2G+g, ... (a snake over rounds), which pairs long items with
-    // short ones.
+    // Persistent, per XCD: token blocks are numbered latest first
+    // (descending work for causal-like windows) and block j belongs to XCD
+    // j % 8, the XCD that runs workgroups g with g % 8 == j % 8 (workgroups
+    // are dispatched to the XCDs round-robin).  Inside an XCD, its blocks'
+    // items are numbered block-major (the chunks of a block are consecutive
+    // items) and its L workgroups take them as a snake over rounds (local
+    // workgroup l: items l, 2L-1-l, 2L+l, ...), which pairs long items with
+    // short ones.  The chunks of a block then run at the same time on the
+    // block's XCD, so its q comes from HBM once and from that XCD's L2 for
+    // the other chunks.
     const int G = (int)gridDim.x, per_chunk = B * n_tblocks;
-    const int n_items = per_chunk * n_chunks;
+    const int nx = (G % kXcds == 0 && per_chunk >= 2 * kXcds) ? kXcds : 1;  // else one group
+    const int x = (int)blockIdx.x % nx, l = (int)blockIdx.x / nx, L = G / nx;
+    const int nbx = (per_chunk - x + nx - 1) / nx;  // blocks of this XCD
+    const int n_items = nbx * n_chunks;
     for (int rnd = 0;; ++rnd) {
-      const int item = rnd * G + ((rnd & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+      const int item = rnd * L + ((rnd & 1) ? L - 1 - l : l);
       if (item >= n_items) break;
       __syncthreads();  // the previous item's LDS reads are complete
-      const int rem = item % per_chunk;
-      process(rem % B, n_tblocks - 1 - rem / B, item / per_chunk);
+      const int rem = (item / n_chunks) * nx + x;  // block number, latest first
+      process(rem % B, n_tblocks - 1 - rem / B, item % n_chunks);
     }
   }
 }
