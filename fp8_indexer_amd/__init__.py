@@ -24,14 +24,16 @@ import os
 
 import torch
 
-__all__ = ["DSAError", "lib", "version", "indexer_logits", "topk", "sparse_attn_fwd",
+__all__ = ["DSAError", "lib", "version", "indexer_logits", "indexer_topk",
+           "indexer_topk_workspace_size", "topk", "sparse_attn_fwd",
            "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
            "prefill_workspace_size", "prefill_noalloc", "KV_BF16", "KV_FP8_E4M3FN",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 KV_BF16, KV_FP8_E4M3FN = 0, 1
-EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
+EXPORTS = ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_indexer_topk_workspace_size",
+           "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_workspace_size", "dsa_prefill", "dsa_prefill_workspace_size",
            "dsa_prefill_noalloc", "dsa_status_string", "dsa_version")
 NOALLOC_SCRATCH_BYTES = 48 << 20  # DSA_NOALLOC_SCRATCH_BYTES
@@ -75,6 +77,11 @@ def lib():
         psz = ctypes.POINTER(ctypes.c_size_t)
         L.dsa_indexer_logits.restype = ctypes.c_int
         L.dsa_indexer_logits.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, P]
+        L.dsa_indexer_topk_workspace_size.restype = ctypes.c_int
+        L.dsa_indexer_topk_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i64, psz]
+        L.dsa_indexer_topk.restype = ctypes.c_int
+        L.dsa_indexer_topk.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i64,
+                                       P, sz, P]
         L.dsa_topk_workspace_size.restype = ctypes.c_int
         L.dsa_topk_workspace_size.argtypes = [i64, i64, i64, i32, psz]
         L.dsa_topk.restype = ctypes.c_int
@@ -205,6 +212,40 @@ def indexer_logits(q, q_scale, k, k_scale, weights, ks, ke, logits=None):
     return logits
 
 
+def indexer_topk_workspace_size(B, M, N, H, D, K, slab_rows=0):
+    """Bytes of scratch dsa_indexer_topk needs (a slab's logits + top-k)."""
+    n = ctypes.c_size_t(0)
+    _check("dsa_indexer_topk_workspace_size", lib().dsa_indexer_topk_workspace_size(
+        B, M, N, H, D, K, slab_rows, ctypes.byref(n)))
+    return n.value
+
+
+def indexer_topk(q, q_scale, k, k_scale, weights, ks, ke, K, out=None, slab_rows=0,
+                 workspace="auto"):
+    """topk_idxs [B,M,K] int32 of the indexer scores, without a [B,M,N]
+    logits buffer (rows are scored and selected in workspace slabs)."""
+    B, M, H, D = _rank(q, "q", 4)
+    N = _rank(k, "k", 3)[1]
+    _tensor(q, "q", _FP8, (B, M, H, D))
+    _tensor(k, "k", _FP8, (B, N, D))
+    _tensor(q_scale, "q_scale", _F32, (B, M, H))
+    _tensor(k_scale, "k_scale", _F32, (B, N))
+    _tensor(weights, "weights", _F32, (B, M, H))
+    _tensor(ks, "ks", _I32, (B, M))
+    _tensor(ke, "ke", _I32, (B, M))
+    _tensor(out, "out", _I32, (B, M, K))
+    _same_device(q, q_scale, k, k_scale, weights, ks, ke, out)
+    if out is None:
+        out = torch.empty((B, M, K), dtype=torch.int32, device=q.device)
+    need = (indexer_topk_workspace_size(B, M, N, H, D, K, slab_rows)
+            if isinstance(workspace, str) else 0)
+    wp, wn, _keep = _workspace(workspace, need, q.device)
+    _check("dsa_indexer_topk", lib().dsa_indexer_topk(
+        _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(weights), _ptr(ks), _ptr(ke),
+        _ptr(out), B, M, N, H, D, K, slab_rows, wp, wn, _stream(q)))
+    return out
+
+
 def topk(logits, ks, ke, K, out=None, workspace="auto"):
     """topk_idxs [B,M,K] int32: ascending selected indices, then -1."""
     B, M, N = _rank(logits, "logits", 3)
@@ -269,14 +310,16 @@ def _prefill_args(index_q, index_q_scale, index_k, index_k_scale, index_weights,
     _tensor(kv, "kv", _FP8 if fp8 else _BF16, (B, N, Dqk))
     _tensor(kv_scale, "kv_scale", _F32, (B, N))
     _tensor(attn_sink, "attn_sink", _F32, (Hq,))
-    _tensor(logits, "logits", _F32, (B, M, N))
+    _tensor(logits if logits is not False else None, "logits", _F32, (B, M, N))
     _tensor(topk_idxs, "topk_idxs", _I32, (B, M, K))
     _tensor(out, "out", _BF16, (B, M, Hq, dv))
     _same_device(q, index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, kv,
-                 kv_scale, attn_sink, logits, topk_idxs, out)
+                 kv_scale, attn_sink, logits if logits is not False else None, topk_idxs, out)
     dev = q.device
     if logits is None:
         logits = torch.empty((B, M, N), dtype=torch.float32, device=dev)
+    elif logits is False:  # slab mode: no [B, M, N] logits buffer
+        logits = None
     if topk_idxs is None:
         topk_idxs = torch.empty((B, M, K), dtype=torch.int32, device=dev)
     if out is None:
@@ -291,7 +334,8 @@ def _prefill_args(index_q, index_q_scale, index_k, index_k_scale, index_weights,
         kv_scale=kv_scale.data_ptr() if fp8 else None,
         attn_sink=attn_sink.data_ptr() if attn_sink is not None else None,
         o=out.data_ptr(), heads=Hq, dqk=Dqk, dv=dv, sm_scale=float(sm_scale),
-        logits=logits.data_ptr(), topk_idxs=topk_idxs.data_ptr(), workspace=None,
+        logits=logits.data_ptr() if logits is not None else None,
+        topk_idxs=topk_idxs.data_ptr(), workspace=None,
         workspace_bytes=0)
     return a, logits, topk_idxs, out
 
@@ -307,7 +351,9 @@ def prefill_workspace_size(args):
 def prefill(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
             attn_sink, sm_scale=0.0, dv=None, kv_scale=None, logits=None, topk_idxs=None,
             out=None, workspace="auto"):
-    """The whole path on the current stream; returns (logits, topk_idxs, o)."""
+    """The whole path on the current stream; returns (logits, topk_idxs, o).
+    logits=False: no [B,M,N] logits buffer (indexer and top-k in workspace
+    slabs); the returned logits is then None."""
     a, logits, topk_idxs, out = _prefill_args(
         index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q, kv,
         attn_sink, sm_scale, dv, kv_scale, logits, topk_idxs, out)

@@ -187,13 +187,144 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv, dsa_kv_dtype kv_dt
 
 namespace {
 
+// ---- indexer + top-k in slabs of rows -------------------------------------
+// The [B, M, N] logits never exist: rows are scored and selected in slabs
+// whose logits live in the workspace.  A slab is a group of whole batch
+// entries (M <= slab rows) or a run of tokens of one batch entry; a tail run
+// too short for the indexer's prefill layout joins the previous run, so
+// every token is scored with the same layout (same summation order) as by
+// one dsa_indexer_logits call over all rows, and the selection, exact by
+// definition, is the same as dsa_topk's on those logits.
+constexpr int64_t kDefaultSlabRows = 2048;
+
+struct Slab {
+  int64_t b0, nb;  // batch entries [b0, b0 + nb)
+  int64_t t0, nt;  // tokens [t0, t0 + nt) of each
+};
+
+// Calls f(slab) for every slab, in row order.
+template <class F>
+void for_each_slab(int64_t B, int64_t M, int H, int64_t slab_rows, F&& f) {
+  if (M <= slab_rows) {
+    const int64_t per = slab_rows / M;
+    for (int64_t b0 = 0; b0 < B; b0 += per) f(Slab{b0, per < B - b0 ? per : B - b0, 0, M});
+    return;
+  }
+  const int64_t tmin = dsa::indexer_prefill_min_tokens(H);
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t0 = 0; t0 < M;) {
+      int64_t nt = M - t0 < slab_rows ? M - t0 : slab_rows;
+      if (M - (t0 + nt) > 0 && M - (t0 + nt) < tmin) nt = M - t0;  // short tail joins
+      f(Slab{b, 1, t0, nt});
+      t0 += nt;
+    }
+}
+
+struct SlabPlan {
+  size_t logits_bytes;  // the largest slab's logits, 256-byte aligned
+  size_t topk_bytes;    // the largest slab's top-k scratch
+  size_t bytes() const { return logits_bytes + topk_bytes; }
+};
+
+int64_t slab_rows_or_default(int64_t slab_rows) {
+  return slab_rows > 0 ? slab_rows : kDefaultSlabRows;
+}
+
+SlabPlan plan_slabs(int64_t B, int64_t M, int64_t N, int H, int K, int64_t slab_rows) {
+  SlabPlan plan{0, 0};
+  for_each_slab(B, M, H, slab_rows, [&](const Slab& sl) {
+    const size_t lb = ((size_t)(sl.nb * sl.nt) * (size_t)N * sizeof(float) + 255) & ~(size_t)255;
+    if (lb > plan.logits_bytes) plan.logits_bytes = lb;
+    const size_t tb = dsa::topk_workspace_bytes(
+        dsa::TopkArgs{nullptr, nullptr, nullptr, nullptr, sl.nb, sl.nt, N, K});
+    if (tb > plan.topk_bytes) plan.topk_bytes = tb;
+  });
+  return plan;
+}
+
+// Every slab: indexer into the workspace's logits, top-k from it.
+dsa_status run_indexer_topk(const dsa::IndexerArgs& ia, int32_t* topk_idxs, int K,
+                            int64_t slab_rows, const SlabPlan& plan, dsa::Workspace ws,
+                            hipStream_t s) {
+  float* slab_logits = static_cast<float*>(ws.ptr);
+  const dsa::Workspace tws{static_cast<char*>(ws.ptr) + plan.logits_bytes,
+                           ws.bytes - plan.logits_bytes};
+  const int64_t M = ia.M, N = ia.N;
+  const int H = ia.H, D = ia.D;
+  dsa_status st = DSA_OK;
+  for_each_slab(ia.B, M, H, slab_rows, [&](const Slab& sl) {
+    if (st != DSA_OK) return;
+    const int64_t r0 = sl.b0 * M + sl.t0;  // first row of the slab
+    dsa::IndexerArgs a = ia;
+    a.q = static_cast<const uint8_t*>(ia.q) + r0 * H * D;
+    a.q_scale = ia.q_scale ? ia.q_scale + r0 * H : nullptr;
+    a.k = static_cast<const uint8_t*>(ia.k) + sl.b0 * N * D;
+    a.k_scale = ia.k_scale + sl.b0 * N;
+    a.w = ia.w + r0 * H;
+    a.ks = ia.ks + r0;
+    a.ke = ia.ke + r0;
+    a.logits = slab_logits;
+    a.B = sl.nb;
+    a.M = sl.nt;
+    st = finish(dsa::launch_indexer(a, s), s);
+    if (st != DSA_OK) return;
+    const dsa::TopkArgs t{slab_logits, a.ks, a.ke, topk_idxs + r0 * K, sl.nb, sl.nt, N, K};
+    st = finish(dsa::launch_topk(t, tws, s), s);
+  });
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_topk_workspace_size(int64_t B, int64_t M, int64_t N, int32_t H, int32_t D,
+                                           int32_t K, int64_t slab_rows, size_t* bytes) {
+  if (!bytes || slab_rows < 0) return DSA_ERR_INVALID_VALUE;
+  alignas(16) static const int64_t dummy[2] = {0, 0};  // stand-in pointers: never dereferenced
+  const float* f = reinterpret_cast<const float*>(dummy);
+  const int32_t* i = reinterpret_cast<const int32_t*>(dummy);
+  dsa_status st = check_indexer(dummy, nullptr, dummy, f, f, i, i, f, B, M, N, H, D);
+  if (st == DSA_OK) st = check_topk(f, i, i, i, B, M, N, K);
+  if (st != DSA_OK) return st;
+  *bytes = plan_slabs(B, M, N, H, K, slab_rows_or_default(slab_rows)).bytes();
+  return DSA_OK;
+}
+
+dsa_status dsa_indexer_topk(const void* q, const float* q_scale, const void* k,
+                            const float* k_scale, const float* weights, const int32_t* ks,
+                            const int32_t* ke, int32_t* topk_idxs, int64_t B, int64_t M,
+                            int64_t N, int32_t H, int32_t D, int32_t K, int64_t slab_rows,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (slab_rows < 0) return DSA_ERR_INVALID_VALUE;
+  const float* dummy = k_scale;  // any non-NULL aligned pointer for the logits check
+  dsa_status st = check_indexer(q, q_scale, k, k_scale, weights, ks, ke, dummy, B, M, N, H, D);
+  if (st == DSA_OK) st = check_topk(dummy, ks, ke, topk_idxs, B, M, N, K);
+  if (st != DSA_OK) return st;
+  const int64_t rows = slab_rows_or_default(slab_rows);
+  const SlabPlan plan = plan_slabs(B, M, N, H, K, rows);
+  if (workspace == nullptr || workspace_bytes < plan.bytes()) return DSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSA_ERR_INVALID_VALUE;
+  const dsa::IndexerArgs ia{q, q_scale, k, k_scale, weights, ks, ke, nullptr, B, M, N, H, D};
+  return run_indexer_topk(ia, topk_idxs, K, rows, plan,
+                          dsa::Workspace{workspace, workspace_bytes},
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
 dsa_status check_prefill(const dsa_prefill_args* p) {
   if (!p) return DSA_ERR_INVALID_VALUE;
+  // logits == NULL selects the slab mode: any non-NULL stand-in passes the
+  // pointer checks below (it is never used)
+  const float* lg = p->logits ? p->logits : p->index_k_scale;
   dsa_status st = check_indexer(p->index_q, p->index_q_scale, p->index_k, p->index_k_scale,
-                                p->index_weights, p->ks, p->ke, p->logits, p->batch, p->seq_q,
+                                p->index_weights, p->ks, p->ke, lg, p->batch, p->seq_q,
                                 p->seq_kv, p->index_heads, p->index_dim);
   if (st == DSA_OK)
-    st = check_topk(p->logits, p->ks, p->ke, p->topk_idxs, p->batch, p->seq_q, p->seq_kv, p->topk);
+    st = check_topk(lg, p->ks, p->ke, p->topk_idxs, p->batch, p->seq_q, p->seq_kv, p->topk);
   if (st == DSA_OK)
     st = check_attn(p->q, p->kv, (int)p->kv_dtype, p->kv_scale, p->attn_sink, p->topk_idxs, p->o,
                     p->batch, p->seq_q, p->seq_kv, p->heads, p->dqk, p->dv, p->topk);
@@ -210,10 +341,16 @@ dsa::AttnArgs prefill_attn_args(const dsa_prefill_args* p) {
                    p->batch, p->seq_q, p->seq_kv, p->heads, p->dqk, p->dv, p->topk, p->sm_scale);
 }
 
-// The top-k and the attention run one after the other on the stream, so
-// they share one workspace.
+SlabPlan prefill_slab_plan(const dsa_prefill_args* p) {
+  return plan_slabs(p->batch, p->seq_q, p->seq_kv, p->index_heads, p->topk, kDefaultSlabRows);
+}
+
+// The stages run one after the other on the stream, so they share one
+// workspace: the larger of the top-k's (or, without a logits buffer, the
+// slabs') and the attention's needs.
 size_t prefill_workspace_bytes(const dsa_prefill_args* p) {
-  const size_t a = dsa::topk_workspace_bytes(prefill_topk_args(p));
+  const size_t a = p->logits ? dsa::topk_workspace_bytes(prefill_topk_args(p))
+                             : prefill_slab_plan(p).bytes();
   const size_t b = dsa::attn_workspace_bytes(prefill_attn_args(p));
   return a > b ? a : b;
 }
@@ -223,9 +360,15 @@ dsa_status run_prefill(const dsa_prefill_args* p, dsa::Workspace ws, hipStream_t
   dsa::IndexerArgs ia{p->index_q, p->index_q_scale, p->index_k, p->index_k_scale,
                       p->index_weights, p->ks, p->ke, p->logits, p->batch, p->seq_q,
                       p->seq_kv, p->index_heads, p->index_dim};
-  dsa_status st = finish(dsa::launch_indexer(ia, s), s);
-  if (st != DSA_OK) return st;
-  st = finish(dsa::launch_topk(prefill_topk_args(p), ws, s), s);
+  dsa_status st;
+  if (p->logits) {
+    st = finish(dsa::launch_indexer(ia, s), s);
+    if (st != DSA_OK) return st;
+    st = finish(dsa::launch_topk(prefill_topk_args(p), ws, s), s);
+  } else {
+    st = run_indexer_topk(ia, p->topk_idxs, p->topk, kDefaultSlabRows, prefill_slab_plan(p), ws,
+                          s);
+  }
   if (st != DSA_OK) return st;
   return finish(dsa::launch_attn(prefill_attn_args(p), ws, s), s);
 }
@@ -245,6 +388,8 @@ dsa_status dsa_prefill_workspace_size(const dsa_prefill_args* p, size_t* bytes) 
 dsa_status dsa_prefill(const dsa_prefill_args* p, void* stream) {
   dsa_status st = check_prefill(p);
   if (st != DSA_OK) return st;
+  if (!p->logits && (p->workspace == nullptr || !aligned(p->workspace, 256)))
+    return p->workspace == nullptr ? DSA_ERR_WORKSPACE : DSA_ERR_INVALID_VALUE;
   st = check_workspace(p->workspace, p->workspace_bytes, prefill_workspace_bytes(p));
   if (st != DSA_OK) return st;
   return run_prefill(p, dsa::Workspace{p->workspace, p->workspace_bytes},

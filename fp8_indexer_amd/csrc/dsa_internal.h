@@ -51,6 +51,11 @@ struct Workspace {
 };
 
 bool indexer_supported(int H, int D);
+
+// Fewest query tokens per batch entry for which the indexer uses its
+// prefill layout (fewer: the key-parallel decode layout, whose head sums
+// are added in another order).
+inline int64_t indexer_prefill_min_tokens(int H) { return 128 / H + 1; }
 bool attn_supported(int Hq, int Dqk, int Dv, bool fp8);
 
 // Compute units of the current device (cached per device, thread-safe).

@@ -487,10 +487,11 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
 // per batch entry with fewer than 128 heads: H / 16 row tiles, no empty rows.
 template <int H, int D>
 hipError_t launch(const IndexerArgs& a, hipStream_t stream) {
+  static_assert(kRowsPerWave == 128, "indexer_prefill_min_tokens assumes 128 rows per wave");
   if constexpr (H >= 16 && H < kRowsPerWave) {
     if (a.M == 1) return launch_kp<H, D, true, H / 16>(a, stream);
   }
-  if (a.M * H <= kRowsPerWave) return launch_kp<H, D, true>(a, stream);
+  if (a.M < indexer_prefill_min_tokens(H)) return launch_kp<H, D, true>(a, stream);
   return launch_kp<H, D, false>(a, stream);
 }
 

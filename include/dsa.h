@@ -142,6 +142,32 @@ dsa_status dsa_topk(const float* logits, const int32_t* ks, const int32_t* ke,
                     void* stream);
 
 /*
+ * dsa_indexer_topk -- dsa_indexer_logits followed by dsa_topk without the
+ * [B, M, N] logits buffer: the pages' planned fused score + top-k-select
+ * step (Modular "sparse_index_fp8_sm100_prefill" page, the paragraph on the
+ * next step: scoring and top-k selection together, with no materialised
+ * [total_seq, max_num_keys] score buffer).  Rows are scored and selected in
+ * slabs of about `slab_rows` rows (0 = 2048) whose logits live in the
+ * workspace: peak scratch is one slab's logits (slab_rows * N * 4 bytes)
+ * plus the top-k's scratch for a slab, instead of B * M * N * 4 bytes.
+ * topk_idxs is exactly what dsa_topk returns on dsa_indexer_logits' output
+ * for the same arguments (same arithmetic per logit; the selection is
+ * exact).  Arguments as in dsa_indexer_logits and dsa_topk.  The
+ * workspace is required (NULL or smaller than
+ * dsa_indexer_topk_workspace_size gives DSA_ERR_WORKSPACE) and must be
+ * 256-byte aligned.
+ */
+dsa_status dsa_indexer_topk_workspace_size(int64_t B, int64_t M, int64_t N, int32_t H,
+                                           int32_t D, int32_t K, int64_t slab_rows,
+                                           size_t* bytes);
+dsa_status dsa_indexer_topk(const void* q, const float* q_scale, const void* k,
+                            const float* k_scale, const float* weights,
+                            const int32_t* ks, const int32_t* ke, int32_t* topk_idxs,
+                            int64_t B, int64_t M, int64_t N, int32_t H, int32_t D,
+                            int32_t K, int64_t slab_rows, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink.
  *
  * Defined by the DeepSeek V4.1 atlas page, sparse_attn_kernel and its wrapper
@@ -194,6 +220,9 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
  * the call only.  The stages run one after the other on `stream`, so one
  * workspace serves both the top-k and the attention:
  * dsa_prefill_workspace_size gives the larger of their needs.
+ * With logits == NULL the indexer and top-k run as dsa_indexer_topk (slabs
+ * of 2048 rows, no [B, M, N] buffer; same topk_idxs); the workspace is then
+ * required and its size includes a slab's logits.
  */
 typedef struct dsa_prefill_args {
   /* sizes */
@@ -224,7 +253,7 @@ typedef struct dsa_prefill_args {
   int32_t dv;                 /* Dv */
   float sm_scale;             /* <= 0 -> 1/sqrt(Dqk) */
   /* caller-owned intermediates */
-  float* logits;              /* [B, M, N] */
+  float* logits;              /* [B, M, N], or NULL: scored in workspace slabs */
   int32_t* topk_idxs;         /* [B, M, K] */
   void* workspace;            /* device scratch or NULL */
   size_t workspace_bytes;
