@@ -15,6 +15,9 @@
  *   attention-- DeepSeek V4.1 atlas page, sparse_attn_kernel and sparse_attn
  *               (gather by index, -1 masked, softmax with a per-head sink in
  *               the denominator only, all-invalid rows give zero).
+ *   backward -- TileLang "deepseek_v32" page, section "Sparse MLA Backward"
+ *               (Delta = rowsum(dO * O), dS = P * (dP - Delta), dQ and the
+ *               scattered dKV), applied to the forward above.
  */
 #include "dsa_oracle.h"
 
@@ -290,6 +293,119 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
     free(rowv);
     free(sc);
     free(qv);
+    free(J);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sparse attention backward                                                 */
+/* ------------------------------------------------------------------------ */
+
+int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
+                               const float* sink, const int32_t* topk_idxs,
+                               const uint16_t* dO, int64_t B, int64_t M,
+                               int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
+                               int32_t K, double sm_scale, const int64_t* rows,
+                               int64_t n_rows, double* dq, double* dkv,
+                               double* dsink, double* tdq, double* tdkv) {
+  if (!q || !kv || !topk_idxs || !dO || !dq || !dkv) return -1;
+  if (sink && !dsink) return -1;
+  if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Dqk <= 0 || Dv <= 0 ||
+      Dv > Dqk || K <= 0)
+    return -1;
+  if (!rows) n_rows = B * M;
+  for (int64_t i = 0; i < n_rows; ++i)
+    if (row_id(rows, i) < 0 || row_id(rows, i) >= B * M) return -1;
+  for (int64_t x = 0; x < B * N * Dqk; ++x) {
+    dkv[x] = 0.0;
+    if (tdkv) tdkv[x] = 0.0;
+  }
+  if (dsink)
+    for (int32_t h = 0; h < Hq; ++h) dsink[h] = 0.0;
+  int failed = 0;
+
+#pragma omp parallel
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)K);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)K);
+    double* qv = (double*)malloc(sizeof(double) * (size_t)Dqk);
+    double* gv = (double*)malloc(sizeof(double) * (size_t)Dv);
+    int32_t* J = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    if (!sc || !dp || !qv || !gv || !J) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      if (!sc || !dp || !qv || !gv || !J) continue;
+      int64_t r = row_id(rows, i);
+      int64_t b = r / M;
+      const int32_t* idx = topk_idxs + r * K;
+      int32_t nj = 0;
+      for (int32_t j = 0; j < K; ++j)
+        if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];
+      for (int32_t h = 0; h < Hq; ++h) {
+        double* g = dq + (i * Hq + h) * (int64_t)Dqk;
+        double* tg = tdq ? tdq + (i * Hq + h) * (int64_t)Dqk : NULL;
+        for (int32_t d = 0; d < Dqk; ++d) {
+          g[d] = 0.0;
+          if (tg) tg[d] = 0.0;
+        }
+        if (nj == 0) continue; /* o = 0 whatever q, kv and the sink */
+        const uint16_t* qh = q + (r * Hq + h) * (int64_t)Dqk;
+        const uint16_t* gh = dO + (r * Hq + h) * (int64_t)Dv;
+        for (int32_t d = 0; d < Dqk; ++d) qv[d] = dsa_oracle_bf16_value(qh[d]);
+        for (int32_t c = 0; c < Dv; ++c) gv[c] = dsa_oracle_bf16_value(gh[c]);
+        /* forward statistics */
+        double mx = -INFINITY;
+        for (int32_t j = 0; j < nj; ++j) {
+          const uint16_t* kr = kv + (b * N + J[j]) * (int64_t)Dqk;
+          double acc = 0.0, dacc = 0.0;
+          for (int32_t d = 0; d < Dqk; ++d) acc += qv[d] * dsa_oracle_bf16_value(kr[d]);
+          for (int32_t c = 0; c < Dv; ++c) dacc += gv[c] * dsa_oracle_bf16_value(kr[c]);
+          sc[j] = sm_scale * acc;
+          dp[j] = dacc;
+          if (sc[j] > mx) mx = sc[j];
+        }
+        double sk = sink ? (double)sink[h] : -INFINITY;
+        if (sk > mx) mx = sk;
+        double den = sink ? exp(sk - mx) : 0.0;
+        for (int32_t j = 0; j < nj; ++j) den += exp(sc[j] - mx);
+        /* Delta = sum_j p_j dp_j */
+        double delta = 0.0;
+        for (int32_t j = 0; j < nj; ++j) delta += exp(sc[j] - mx) / den * dp[j];
+        if (sink) {
+          double ps = exp(sk - mx) / den;
+#pragma omp atomic
+          dsink[h] += -ps * delta;
+        }
+        for (int32_t j = 0; j < nj; ++j) {
+          double p = exp(sc[j] - mx) / den;
+          double ds = p * (dp[j] - delta);
+          const uint16_t* kr = kv + (b * N + J[j]) * (int64_t)Dqk;
+          double* gk = dkv + (b * N + J[j]) * (int64_t)Dqk;
+          double* tk = tdkv ? tdkv + (b * N + J[j]) * (int64_t)Dqk : NULL;
+          for (int32_t d = 0; d < Dqk; ++d) {
+            double kvd = dsa_oracle_bf16_value(kr[d]);
+            g[d] += sm_scale * ds * kvd;
+            if (tg) tg[d] += sm_scale * fabs(ds) * fabs(kvd);
+            double add = sm_scale * ds * qv[d] + (d < Dv ? p * gv[d] : 0.0);
+#pragma omp atomic
+            gk[d] += add;
+            if (tk) {
+              double tadd = sm_scale * fabs(ds) * fabs(qv[d]) + (d < Dv ? p * fabs(gv[d]) : 0.0);
+#pragma omp atomic
+              tk[d] += tadd;
+            }
+          }
+        }
+      }
+    }
+    free(sc);
+    free(dp);
+    free(qv);
+    free(gv);
     free(J);
   }
   return failed ? -1 : 0;

@@ -84,6 +84,33 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
                            int32_t K, double sm_scale, const int64_t* rows,
                            int64_t n_rows, double* o);
 
+/* Gradients of that sparse attention (TileLang deepseek_v32 page, "Sparse
+ * MLA Backward": dP from dO and V, Delta = rowsum(dO * O), dS = P * (dP -
+ * Delta), dQ from dS and K, dKV scattered back to the gathered rows).  For
+ * each listed (b,t) and head h, with p_j = exp(s_j - Mx) / den and p_sink =
+ * exp(sink_h - Mx) / den as in the forward:
+ *   dp_j      = sum_{c<Dv} dO[b,t,h,c] * kv[b,j,c]
+ *   Delta     = sum_j p_j * dp_j              (= sum_c dO[c] * o[c])
+ *   ds_j      = p_j * (dp_j - Delta)
+ *   dq[d]     = sm_scale * sum_j ds_j * kv[b,j,d]               d < Dqk
+ *   dkv[b,j,d] += sm_scale * ds_j * q[d] + (d < Dv ? p_j * dO[d] : 0)
+ *   dsink[h]  += -p_sink * Delta
+ * Each occurrence of a duplicated index contributes; rows without a valid
+ * index contribute nothing.  q, kv, dO are bf16 bits.
+ *   dq    [n_rows, Hq, Dqk] fp64 (listed rows)
+ *   dkv   [B, N, Dqk] fp64: the listed rows' contributions (overwritten)
+ *   dsink [Hq] fp64 (listed rows), or NULL when sink is NULL
+ *   tdq, tdkv: NULL, or the same shapes holding the sums of the absolute
+ *   values of the terms above (sm_scale |ds_j| |kv_j[d]|, and sm_scale
+ *   |ds_j| |q[d]| + p_j |dO[d]|), for tolerances.                          */
+int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
+                               const float* sink, const int32_t* topk_idxs,
+                               const uint16_t* dO, int64_t B, int64_t M,
+                               int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
+                               int32_t K, double sm_scale, const int64_t* rows,
+                               int64_t n_rows, double* dq, double* dkv,
+                               double* dsink, double* tdq, double* tdkv);
+
 /* Number of OpenMP threads the oracle runs with (0 if built without). */
 int dsa_oracle_num_threads(void);
 

@@ -491,10 +491,113 @@ def check_rows_subsets(seed=31):
     assert np.allclose(got3, dense[rows3], rtol=1e-12, atol=1e-12), "attention rows"
 
 
+# -------------------------------------------------------------- backward --
+
+def _attn_multiset(qv, kvv, sink, idx, sm_scale, dv):
+    """Forward of the sparse attention in numpy fp64, looping over index
+    occurrences (a duplicated index counts each time), for finite differences
+    of the backward; independent of the oracle's C code."""
+    B, M, Hq, Dqk = qv.shape
+    N = kvv.shape[1]
+    out = np.zeros((B * M, Hq, dv))
+    for b in range(B):
+        for t in range(M):
+            J = [int(j) for j in idx[b, t] if 0 <= j < N]
+            if not J:
+                continue
+            for h in range(Hq):
+                s = np.array([sm_scale * float(qv[b, t, h] @ kvv[b, j]) for j in J])
+                mx = max(s.max(), sink[h] if sink is not None else -np.inf)
+                e = np.exp(s - mx)
+                den = e.sum() + (np.exp(sink[h] - mx) if sink is not None else 0.0)
+                out[b * M + t, h] = sum(e[k] * kvv[b, J[k], :dv] for k in range(len(J))) / den
+    return out
+
+
+def check_attn_bwd_finite_differences(seed=41):
+    """Oracle gradients of L = sum(dO * o) against central differences of the
+    numpy forward, for every element of q, kv and the sink, with duplicated
+    and -1 indices, with and without a sink."""
+    rng = np.random.default_rng(seed)
+    B, M, N, Hq, Dqk, Dv, K = 1, 3, 6, 2, 5, 4, 5
+    for with_sink in (True, False):
+        qb = _bf16_bits(rng.standard_normal((B, M, Hq, Dqk)))
+        kvb = _bf16_bits(rng.standard_normal((B, N, Dqk)))
+        gb = _bf16_bits(rng.standard_normal((B, M, Hq, Dv)))
+        sink = rng.standard_normal(Hq).astype(np.float32) if with_sink else None
+        idx = np.array([[[0, 3, 3, -1, 5], [2, -1, -1, 4, 1], [-1, -1, -1, -1, -1]]], np.int32)
+        qv = _torch_bf16(qb.view(np.uint16).ravel()).reshape(qb.shape)
+        kvv = _torch_bf16(kvb.view(np.uint16).ravel()).reshape(kvb.shape)
+        gv = _torch_bf16(gb.view(np.uint16).ravel()).reshape(gb.shape)
+        sc = 0.4
+        dq, dkv, dsink = oracle.sparse_attn_bwd(qb, kvb, sink, idx, gb, sc, Dv)
+        sk64 = None if sink is None else sink.astype(np.float64)
+
+        def loss(qx, kx, sx):
+            return float((_attn_multiset(qx, kx, sx, idx, sc, Dv) *
+                          gv.reshape(B * M, Hq, Dv)).sum())
+
+        eps = 1e-6
+        for arr, grad, name in ((qv, dq.reshape(qv.shape), "q"), (kvv, dkv, "kv")):
+            for pos in np.ndindex(arr.shape):
+                a1, a2 = arr.copy(), arr.copy()
+                a1[pos] += eps
+                a2[pos] -= eps
+                args1 = (a1, kvv, sk64) if name == "q" else (qv, a1, sk64)
+                args2 = (a2, kvv, sk64) if name == "q" else (qv, a2, sk64)
+                fd = (loss(*args1) - loss(*args2)) / (2 * eps)
+                assert abs(fd - grad[pos]) <= 1e-6 * (1 + abs(fd)), (name, pos, fd, grad[pos])
+        if sink is not None:
+            for h in range(Hq):
+                s1, s2 = sk64.copy(), sk64.copy()
+                s1[h] += eps
+                s2[h] -= eps
+                fd = (loss(qv, kvv, s1) - loss(qv, kvv, s2)) / (2 * eps)
+                assert abs(fd - dsink[h]) <= 1e-6 * (1 + abs(fd)), ("sink", h, fd, dsink[h])
+        else:
+            assert dsink is None
+
+
+def check_attn_bwd_closed_forms(seed=42):
+    """One valid index and no sink: p = 1, so dS = 0 (dq = 0) and the row's
+    dkv is dO on the first Dv columns, 0 beyond; a row without a valid index
+    contributes nothing; -1 padding changes nothing; rows= lists the
+    contributions of the listed rows only."""
+    rng = np.random.default_rng(seed)
+    B, M, N, Hq, Dqk, Dv, K = 1, 2, 5, 3, 6, 4, 4
+    qb = _bf16_bits(rng.standard_normal((B, M, Hq, Dqk)))
+    kvb = _bf16_bits(rng.standard_normal((B, N, Dqk)))
+    gb = _bf16_bits(rng.standard_normal((B, M, Hq, Dv)))
+    gv = _torch_bf16(gb.view(np.uint16).ravel()).reshape(gb.shape)
+    idx = np.array([[[2, -1, -1, -1], [-1, -1, -1, -1]]], np.int32)
+    dq, dkv, _ = oracle.sparse_attn_bwd(qb, kvb, None, idx, gb, 0.5, Dv)
+    assert np.all(dq == 0.0)
+    want = np.zeros((B, N, Dqk))
+    want[0, 2, :Dv] = gv[0, 0].sum(axis=0)  # every head's dO lands on row 2
+    assert np.allclose(dkv, want, rtol=0, atol=1e-15), np.abs(dkv - want).max()
+    # padding with -1 and a second copy of the idx layout give the same result
+    idx2 = np.array([[[-1, 4, 1, -1], [3, 0, -1, -1]]], np.int32)
+    sink = rng.standard_normal(Hq).astype(np.float32)
+    a = oracle.sparse_attn_bwd(qb, kvb, sink, idx2, gb, 0.5, Dv)
+    idx3 = np.concatenate([idx2, np.full((B, M, 3), -1, np.int32)], axis=2)
+    b_ = oracle.sparse_attn_bwd(qb, kvb, sink, idx3, gb, 0.5, Dv)
+    for x, y in zip(a, b_):
+        assert np.array_equal(x, y)
+    # rows=[1] equals the full call with row 0's dO set to zero
+    r1 = oracle.sparse_attn_bwd(qb, kvb, sink, idx2, gb, 0.5, Dv, rows=[1])
+    g0 = gb.copy()
+    g0[0, 0] = 0
+    full0 = oracle.sparse_attn_bwd(qb, kvb, sink, idx2, g0, 0.5, Dv)
+    assert np.allclose(r1[0], full0[0][1:], rtol=1e-13, atol=1e-15)
+    assert np.allclose(r1[1], full0[1], rtol=1e-13, atol=1e-15)
+    assert np.allclose(r1[2], full0[2], rtol=1e-13, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_e4m3_decode, check_bf16_decode,
     check_indexer_hand, check_indexer_exact, check_indexer_invariants, check_indexer_terms,
     check_topk_hand, check_topk_bruteforce, check_topk_invariants,
     check_attn_hand, check_attn_dense, check_attn_closed_forms, check_attn_invariants,
     check_attn_fp8_kv, check_rows_subsets,
+    check_attn_bwd_finite_differences, check_attn_bwd_closed_forms,
 ]

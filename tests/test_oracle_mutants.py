@@ -31,20 +31,30 @@ MUTANTS = [
     ("topk_not_sorted", "qsort(o, (size_t)K, sizeof(int32_t), cmp_int_asc);", ";"),
     ("topk_short_row_offset", "o[j] = (int32_t)(s + j);", "o[j] = (int32_t)j;"),
     ("sink_dropped", "if (sink) den += exp(sk - mx);", ";"),
-    ("sink_scaled", "double sk = sink ? (double)sink[h] : -INFINITY;",
-     "double sk = sink ? sm_scale * (double)sink[h] : -INFINITY;"),
+    ("sink_scaled", "double sk = sink ? (double)sink[h] : -INFINITY;\n        if (sk > mx) mx = sk;\n        double den = 0.0;",
+     "double sk = sink ? sm_scale * (double)sink[h] : -INFINITY;\n        if (sk > mx) mx = sk;\n        double den = 0.0;"),
     ("v_wrong_slice", "oh[c] += p * vr[c];", "oh[c] += p * vr[c + (Dqk - Dv)];"),
-    ("scale_ignored", "sc[j] = sm_scale * acc;", "sc[j] = acc;"),
-    ("minus_one_not_masked", "if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];",
-     "if (idx[j] < N) J[nj++] = idx[j] < 0 ? 0 : idx[j];"),
+    ("scale_ignored", "sc[j] = sm_scale * acc;\n          if (sc[j] > mx)", "sc[j] = acc;\n          if (sc[j] > mx)"),
+    ("minus_one_not_masked", "if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      /* decode",
+     "if (idx[j] < N) J[nj++] = idx[j] < 0 ? 0 : idx[j];\n      /* decode"),
+    ("bwd_minus_one_not_masked", "if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      for (int32_t h",
+     "if (idx[j] < N) J[nj++] = idx[j] < 0 ? 0 : idx[j];\n      for (int32_t h"),
     ("fp8_kv_scale_ignored", "(double)kv_scale[b * N + J[j]];", "1.0;"),
     # row-subset paths: the listed row's own window / query / index list
     ("topk_rows_window", "window(ks, ke, r, N, &s, &e);\n      int32_t* o = out + i * K;",
      "window(ks, ke, i, N, &s, &e);\n      int32_t* o = out + i * K;"),
     ("indexer_rows_query", "const uint8_t* qr = q + (r * H + h) * D;",
      "const uint8_t* qr = q + (i * H + h) * D;"),
-    ("attn_rows_indices", "const int32_t* idx = topk_idxs + r * K;",
-     "const int32_t* idx = topk_idxs + i * K;"),
+    ("attn_rows_indices", "const int32_t* idx = topk_idxs + r * K;\n      int32_t nj = 0;\n      for (int32_t j = 0; j < K; ++j)\n        if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      /* decode",
+     "const int32_t* idx = topk_idxs + i * K;\n      int32_t nj = 0;\n      for (int32_t j = 0; j < K; ++j)\n        if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      /* decode"),
+    # backward
+    ("bwd_delta_dropped", "double ds = p * (dp[j] - delta);", "double ds = p * dp[j];"),
+    ("bwd_dq_unscaled", "g[d] += sm_scale * ds * kvd;", "g[d] += ds * kvd;"),
+    ("bwd_dv_dropped", "(d < Dv ? p * gv[d] : 0.0);\n#pragma omp atomic\n            gk[d] += add;",
+     "0.0;\n#pragma omp atomic\n            gk[d] += add;"),
+    ("bwd_dk_wrong_q", "double add = sm_scale * ds * qv[d]", "double add = sm_scale * ds * kvd"),
+    ("bwd_dsink_sign", "dsink[h] += -ps * delta;", "dsink[h] += ps * delta;"),
+    ("bwd_sink_in_max_only", "double den = sink ? exp(sk - mx) : 0.0;", "double den = 0.0;"),
 ]
 
 
