@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["DSAError", "lib", "version", "indexer_logits", "indexer_topk",
-           "indexer_topk_workspace_size", "topk", "sparse_attn_fwd",
+           "indexer_topk_workspace_size", "topk", "sparse_attn_fwd", "sparse_attn_bwd",
            "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
            "prefill_workspace_size", "prefill_noalloc", "KV_BF16", "KV_FP8_E4M3FN",
            "LIB_PATH"]
@@ -35,7 +35,7 @@ KV_BF16, KV_FP8_E4M3FN = 0, 1
 EXPORTS = ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_indexer_topk_workspace_size",
            "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_workspace_size", "dsa_prefill", "dsa_prefill_workspace_size",
-           "dsa_prefill_noalloc", "dsa_status_string", "dsa_version")
+           "dsa_prefill_noalloc", "dsa_sparse_attn_bwd", "dsa_status_string", "dsa_version")
 NOALLOC_SCRATCH_BYTES = 48 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -91,6 +91,9 @@ def lib():
         L.dsa_sparse_attn_fwd.restype = ctypes.c_int
         L.dsa_sparse_attn_fwd.argtypes = [P, P, ctypes.c_int, P, P, P, P, i64, i64, i64, i32,
                                           i32, i32, i32, ctypes.c_float, P, sz, P]
+        L.dsa_sparse_attn_bwd.restype = ctypes.c_int
+        L.dsa_sparse_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32,
+                                          i32, i32, ctypes.c_float, P]
         L.dsa_prefill_workspace_size.restype = ctypes.c_int
         L.dsa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs), psz]
         L.dsa_prefill.restype = ctypes.c_int
@@ -289,6 +292,39 @@ def sparse_attn_fwd(q, kv, attn_sink, topk_idxs, sm_scale=0.0, dv=None, kv_scale
             _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, M, N, Hq, Dqk, dv, K,
             float(sm_scale), wp, wn, _stream(q)))
     return out
+
+
+def sparse_attn_bwd(q, kv, attn_sink, topk_idxs, o, dO, sm_scale=0.0, dq=None, dkv=None,
+                    dsink=None):
+    """Gradients (dq [B,M,Hq,Dqk], dkv [B,N,Dqk], dsink [Hq] or None), fp32,
+    of dsa_sparse_attn_fwd with bf16 kv; o is the forward's output."""
+    B, M, Hq, Dqk = _rank(q, "q", 4)
+    N = _rank(kv, "kv", 3)[1]
+    K = _rank(topk_idxs, "topk_idxs", 3)[2]
+    Dv = _rank(dO, "dO", 4)[3]
+    _tensor(q, "q", _BF16, (B, M, Hq, Dqk))
+    _tensor(kv, "kv", _BF16, (B, N, Dqk))
+    _tensor(attn_sink, "attn_sink", _F32, (Hq,))
+    _tensor(topk_idxs, "topk_idxs", _I32, (B, M, K))
+    _tensor(o, "o", _BF16, (B, M, Hq, Dv))
+    _tensor(dO, "dO", _BF16, (B, M, Hq, Dv))
+    _tensor(dq, "dq", _F32, (B, M, Hq, Dqk))
+    _tensor(dkv, "dkv", _F32, (B, N, Dqk))
+    _tensor(dsink, "dsink", _F32, (Hq,))
+    _same_device(q, kv, attn_sink, topk_idxs, o, dO, dq, dkv, dsink)
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((B, M, Hq, Dqk), dtype=torch.float32, device=dev)
+    if dkv is None:
+        dkv = torch.empty((B, N, Dqk), dtype=torch.float32, device=dev)
+    if attn_sink is not None and dsink is None:
+        dsink = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    if attn_sink is None:
+        dsink = None
+    _check("dsa_sparse_attn_bwd", lib().dsa_sparse_attn_bwd(
+        _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), _ptr(o), _ptr(dO), _ptr(dq),
+        _ptr(dkv), _ptr(dsink), B, M, N, Hq, Dqk, Dv, K, float(sm_scale), _stream(q)))
+    return dq, dkv, dsink
 
 
 def _prefill_args(index_q, index_q_scale, index_k, index_k_scale, index_weights, ks, ke, K, q,

@@ -377,6 +377,27 @@ dsa_status run_prefill(const dsa_prefill_args* p, dsa::Workspace ws, hipStream_t
 
 extern "C" {
 
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const float* attn_sink,
+                               const int32_t* topk_idxs, const void* o, const void* dO,
+                               float* dq, float* dkv, float* dsink, int64_t B, int64_t M,
+                               int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K,
+                               float sm_scale, void* stream) {
+  if (!q || !kv || !topk_idxs || !o || !dO || !dq || !dkv) return DSA_ERR_INVALID_VALUE;
+  if ((attn_sink == nullptr) != (dsink == nullptr)) return DSA_ERR_INVALID_VALUE;
+  if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Dqk <= 0 || Dv <= 0 || K <= 0 || Dv > Dqk)
+    return DSA_ERR_INVALID_VALUE;
+  if (B * M > kMaxI32 || N > kMaxI32 || B > kMaxI32 / N) return DSA_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dkv, 16) || !aligned(topk_idxs, 4) ||
+      (attn_sink && !aligned(attn_sink, 4)) || (dsink && !aligned(dsink, 4)))
+    return DSA_ERR_INVALID_VALUE;
+  if (K > 4096 || !dsa::attn_bwd_supported(Hq, Dqk, Dv)) return DSA_ERR_NOT_SUPPORTED;
+  const dsa::AttnBwdArgs a{q, kv, attn_sink, topk_idxs, o, dO, dq, dkv, dsink,
+                           B, M, N, Hq, Dqk, Dv, K, sm_scale};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(dsa::launch_attn_bwd(a, s), s);
+}
+
 dsa_status dsa_prefill_workspace_size(const dsa_prefill_args* p, size_t* bytes) {
   if (!bytes) return DSA_ERR_INVALID_VALUE;
   const dsa_status st = check_prefill(p);

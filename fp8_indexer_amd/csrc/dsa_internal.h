@@ -50,7 +50,23 @@ struct Workspace {
   size_t bytes;
 };
 
+struct AttnBwdArgs {
+  const void* q;
+  const void* kv;
+  const float* attn_sink;
+  const int32_t* topk_idxs;
+  const void* o;
+  const void* dO;
+  float* dq;
+  float* dkv;
+  float* dsink;
+  int64_t B, M, N;
+  int Hq, Dqk, Dv, K;
+  float sm_scale;
+};
+
 bool indexer_supported(int H, int D);
+bool attn_bwd_supported(int Hq, int Dqk, int Dv);
 
 // Fewest query tokens per batch entry for which the indexer uses its
 // prefill layout (fewer: the key-parallel decode layout, whose head sums
@@ -70,5 +86,6 @@ size_t attn_workspace_bytes(const AttnArgs& a);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, Workspace ws, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
 }  // namespace dsa

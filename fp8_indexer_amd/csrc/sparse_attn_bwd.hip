@@ -1,0 +1,357 @@
+// sparse_attn_bwd.hip -- gradients of the gathered sparse attention with a
+// sink, gfx950.
+//
+// Method (TileLang "deepseek_v32" page, "Sparse MLA Backward"), for each query
+// token and head, over the gathered rows j of its top-k list:
+//   p_j   = exp(s_j - lse)           (lse of the forward, sink included)
+//   dp_j  = dO . V_j                 (V_j: the first Dv columns of row j)
+//   Delta = dO . o                   (o: the forward output)
+//   ds_j  = p_j (dp_j - Delta)
+//   dq    = sm_scale sum_j ds_j kv_j
+//   dkv_j += sm_scale ds_j q + p_j dO (first Dv columns), scattered to row j
+//   dsink -= p_sink Delta
+//
+// Design (MI355X-first):
+//  * One workgroup per (query token, group of 16 heads), 4 waves that take
+//    the token's 16-row tiles in turn (wave w: tiles w, w+4, ...), each
+//    gathering its own tiles into its own LDS buffer, so the waves never
+//    wait for each other inside the loops.
+//  * Pass 1 recomputes lse: S^T = KV.Q^T on v_mfma_f32_16x16x32_bf16 (q
+//    B-fragments in VGPRs), an online max / sum per head, combined over the
+//    lane groups and the waves, with the sink.
+//  * Pass 2 per tile: S^T and dP^T = V.dO^T in the MFMA C layout (a lane
+//    holds one head and 4 gathered rows), ds and p in registers; then
+//      dq^T  += KV^T dS^T on v_mfma_f32_16x16x16_bf16: the C layout of dS^T
+//               is its B-fragment, KV^T comes from the row-major tile through
+//               the transposing LDS read (ds_read_b64_tr_b16); the 36 dq^T
+//               tiles stay in AGPRs for the whole token;
+//      dkv   = [scale dS | P] [q ; dO] on v_mfma_f32_16x16x32_bf16 with the
+//               16 heads of dS and the 16 heads of P as the 32-deep k
+//               dimension: A from a small LDS transpose of dS and P, B read
+//               transposed from q and dO in LDS; each 16x16 block is added to
+//               the gathered rows of dkv with fp32 atomics (rows repeat across
+//               tokens: the scatter of the pages' backward).
+//  * dq, dkv and dsink accumulate in fp32 (dq and dsink with atomics over
+//    the waves and head groups); the entry point zero-fills them first.
+//  * Invalid indices (-1 or outside [0, N)) gather nothing, have p = 0 and
+//    add nothing.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+typedef short bs4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bs4 lds_bs4;
+
+__device__ __forceinline__ bs4 tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bs4*)(p));
+}
+
+// D = A*B + C on a 16x16 fp32 tile, A/B 16x16 bf16 (4 values per lane):
+// lane l holds A row l%16, k = 4(l/16)..+3; B column l%16, same k.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(const bs4& a, const bs4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int DQK, int DV>
+struct BwdCfg {
+  static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "dims");
+  static constexpr int NW = 4;            // waves per workgroup
+  static constexpr int THREADS = NW * kWave;
+  static constexpr int HG = 16;           // heads per workgroup
+  static constexpr int TR = 16;           // gathered rows per tile
+  // LDS row strides (elements): odd numbers of 32-byte pairs, as in the
+  // forward kernel, so that transposing reads of 4 rows x 32 bytes fill the
+  // banks and 16-row 16-byte reads run at full rate
+  static constexpr int RS = DQK + 16;
+  static constexpr int GS = DV + 16;
+  static_assert((RS * 2 / 32) % 2 == 1 && (GS * 2 / 32) % 2 == 1, "strides");
+  static constexpr int KC = DQK / 32;     // 32-deep k-steps of S
+  static constexpr int VC = DV / 32;      // 32-deep k-steps of dP
+  static constexpr int DT = DQK / 16;     // 16-wide column tiles of dq / dkv
+  static constexpr int VT = DV / 16;      // of which the first VT get the P.dO part
+  static constexpr int CPR = DQK / 8;     // 16-byte chunks per kv row
+  static constexpr int CPL = (TR * CPR + kWave - 1) / kWave;  // chunks per lane and tile
+  static constexpr int TS = 40;           // row stride of the dS|P transpose (elements)
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const float* __restrict__ sink, const int* __restrict__ idx, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dkv,
+    float* __restrict__ dsink, int M, int N, int Hq, int K, float scale, float scale_log2) {
+  using C = BwdCfg<DQK, DV>;
+  constexpr int NW = C::NW, TR = C::TR, RS = C::RS, GS = C::GS;
+  __shared__ __align__(16) uint16_t sKV[NW][TR * RS];
+  __shared__ __align__(16) uint16_t sQ[16 * RS];
+  __shared__ __align__(16) uint16_t sG[16 * GS];
+  __shared__ __align__(16) uint16_t sT[NW][TR * C::TS];
+  __shared__ int sIdx[NW][TR];
+  __shared__ float sM[NW][16], sL[NW][16], sDelta[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, col = lane & 15;
+  const int hgs = Hq / 16;
+  const int r = (int)(blockIdx.x / hgs);           // (b, t) row
+  const int h0 = (int)(blockIdx.x % hgs) * 16;     // first head of the group
+  const int b = r / M;
+  const int* ridx = idx + (size_t)r * K;
+  const int ntiles = (K + TR - 1) / TR;
+
+  // ---- q and dO rows of the 16 heads into LDS; Delta = dO . o per head ----
+  {
+    const uint16_t* qg = q + ((size_t)r * Hq + h0) * DQK;
+    for (int u = tid; u < 16 * (DQK / 8); u += C::THREADS) {
+      const int hh = u / (DQK / 8), c8 = u % (DQK / 8);
+      *reinterpret_cast<i32x4*>(&sQ[hh * RS + c8 * 8]) =
+          *reinterpret_cast<const i32x4*>(qg + (size_t)hh * DQK + c8 * 8);
+    }
+    const uint16_t* gg = dO + ((size_t)r * Hq + h0) * DV;
+    for (int u = tid; u < 16 * (DV / 8); u += C::THREADS) {
+      const int hh = u / (DV / 8), c8 = u % (DV / 8);
+      *reinterpret_cast<i32x4*>(&sG[hh * GS + c8 * 8]) =
+          *reinterpret_cast<const i32x4*>(gg + (size_t)hh * DV + c8 * 8);
+    }
+    // wave w: heads 4w..4w+3, 16 lanes per head
+    const int hh = wave * 4 + g;
+    const uint16_t* orow = o + ((size_t)r * Hq + h0 + hh) * DV;
+    const uint16_t* grow = gg + (size_t)hh * DV;
+    float acc = 0.f;
+    for (int c = col; c < DV; c += 16)
+      acc += __uint_as_float((uint32_t)orow[c] << 16) * __uint_as_float((uint32_t)grow[c] << 16);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+    if (col == 0) sDelta[hh] = acc;
+  }
+  __syncthreads();
+
+  // q B-fragments (S^T = KV.Q^T): head col, k-step c: columns 32c + 8g..+7
+  bf16x8 qf[C::KC];
+#pragma unroll
+  for (int c = 0; c < C::KC; ++c)
+    qf[c] = *reinterpret_cast<const bf16x8*>(&sQ[col * RS + c * 32 + g * 8]);
+
+  // ---- gathering a tile: 16 rows of this wave's tile `it` into sKV[wave] ----
+  uint16_t* kvt = sKV[wave];
+  auto stage = [&](int it) {
+    if (lane < TR) {
+      const int p = it * TR + lane;
+      const int v = p < K ? ridx[p] : -1;
+      sIdx[wave][lane] = (v >= 0 && v < N) ? v : -1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // invalid slots gather row 0 of the batch entry (finite data; their p
+    // and ds are 0 and their dkv is not written), so every load is issued
+    // unconditionally, before the first wait
+    static_assert(C::CPL * kWave == TR * C::CPR, "whole chunks per lane");
+    i32x4 buf[C::CPL];
+#pragma unroll
+    for (int k = 0; k < C::CPL; ++k) {
+      const int ch = lane + k * kWave;
+      const int j = max(sIdx[wave][ch / C::CPR], 0);
+      buf[k] = *reinterpret_cast<const i32x4*>(kv + ((size_t)b * N + j) * DQK + (ch % C::CPR) * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < C::CPL; ++k) {
+      const int ch = lane + k * kWave;
+      *reinterpret_cast<i32x4*>(&kvt[(ch / C::CPR) * RS + (ch % C::CPR) * 8]) = buf[k];
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  // S^T of the current tile in the C layout: lane (col = head, g) holds rows
+  // 4g + i; scores in log2 units, -inf for invalid rows
+  auto scores = [&](float (&s2)[4]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kvt[col * RS + c * 32 + g * 8]);
+      acc = mfma_bf16_16x16x32(a, qf[c], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s2[i] = sIdx[wave][4 * g + i] >= 0 ? acc[i] * scale_log2 : -INFINITY;
+  };
+
+  // ---- pass 1: lse per head (log2 units) ------------------------------------
+  float mrun = -INFINITY, lrun = 0.f;  // per lane: its head, its rows
+  for (int it = wave; it < ntiles; it += NW) {
+    stage(it);
+    float s2[4];
+    scores(s2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (s2[i] == -INFINITY) continue;  // invalid row
+      if (s2[i] > mrun) {
+        lrun = lrun * fast_exp2(mrun - s2[i]);  // 0 * 0 while mrun is -inf
+        mrun = s2[i];
+      }
+      lrun += fast_exp2(s2[i] - mrun);
+    }
+  }
+  // combine the four lane groups of each head, then the waves
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {
+    const float mo = __shfl_xor(mrun, m, kWave), lo = __shfl_xor(lrun, m, kWave);
+    const float mn = fmaxf(mrun, mo);
+    lrun = (mrun == -INFINITY ? 0.f : lrun * fast_exp2(mrun - mn)) +
+           (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - mn));
+    mrun = mn;
+  }
+  if (g == 0) {
+    sM[wave][col] = mrun;
+    sL[wave][col] = lrun;
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sM[w][col]);
+  const float sink2 = sink ? sink[h0 + col] * kLog2eB : -INFINITY;
+  const bool any = mx > -INFINITY;  // the row has a valid index
+  float lse2 = 0.f, psink = 0.f;
+  const float delta = sDelta[col];
+  if (any) {
+    const float m2 = fmaxf(mx, sink2);
+    float l = sink ? fast_exp2(sink2 - m2) : 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      l += sM[w][col] == -INFINITY ? 0.f : sL[w][col] * fast_exp2(sM[w][col] - m2);
+    lse2 = m2 + __log2f(l);
+    psink = sink ? fast_exp2(sink2 - lse2) : 0.f;
+  }
+  if (wave == 0 && g == 0 && sink && any) unsafeAtomicAdd(dsink + h0 + col, -psink * delta);
+  if (!any) return;  // uniform over the workgroup: no gradient at all
+
+  // ---- pass 2 ----------------------------------------------------------------
+  f32x4 dqa[C::DT];  // dq^T tiles: lane (col = head, g) holds columns 16t + 4g + i
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t) dqa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* st = sT[wave];
+  // transposing-read offsets: 4x16 blocks, lane (col) -> row col/4, column 4(col%4)
+  const int trr = col >> 2, trc = 4 * (col & 3);
+  for (int it = wave; it < ntiles; it += NW) {
+    stage(it);
+    float s2[4];
+    scores(s2);
+    // dP^T = V.dO^T
+    f32x4 dpa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::VC; ++c) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kvt[col * RS + c * 32 + g * 8]);
+      const bf16x8 bg = *reinterpret_cast<const bf16x8*>(&sG[col * GS + c * 32 + g * 8]);
+      dpa = mfma_bf16_16x16x32(a, bg, dpa);
+    }
+    // p and ds of rows 4g + i for this lane's head
+    float p[4], ds[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(s2[i] - lse2);  // 0 for an invalid row
+      ds[i] = p[i] * (dpa[i] - delta);
+    }
+    // dq^T += KV^T dS^T (k = the tile's 16 rows): B = dS^T in the C layout
+    const bs4 dsb = __builtin_bit_cast(
+        bs4, __builtin_convertvector(f32x4{ds[0], ds[1], ds[2], ds[3]}, bf16x4));
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) {
+      const bs4 a = tr16(&kvt[(4 * g + trr) * RS + 16 * t + trc]);
+      dqa[t] = mfma_bf16_16x16x16(a, dsb, dqa[t]);
+    }
+    // dS and P transposed through LDS: st[j][k], k < 16: scale * ds of head
+    // k, k >= 16: p of head k - 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st[(4 * g + i) * C::TS + col] = __builtin_bit_cast(uint16_t, (__bf16)(scale * ds[i]));
+      st[(4 * g + i) * C::TS + 16 + col] = __builtin_bit_cast(uint16_t, (__bf16)p[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // dkv[j, d] = sum_k A[j, k] B[k, d]: A row col, k = 8g..8g+7
+    const bf16x8 aT = *reinterpret_cast<const bf16x8*>(&st[col * C::TS + 8 * g]);
+    int jrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) jrow[i] = sIdx[wave][4 * g + i];
+#pragma unroll 4
+    for (int t = 0; t < C::DT; ++t) {
+      // B row block k = 8g..8g+7: q heads (g < 2) or dO heads (g >= 2), column
+      // 16t + col; two transposing reads of 4 heads each
+      // (every lane reads; the dO columns past Dv are read in range and
+      // replaced by zeros)
+      const bool from_q = g < 2;
+      const uint16_t* bp = from_q ? &sQ[(8 * g + trr) * RS + 16 * t + trc]
+                                  : &sG[(8 * (g - 2) + trr) * GS +
+                                        16 * (t < C::VT ? t : C::VT - 1) + trc];
+      const int stride = from_q ? RS : GS;
+      bs4 lo = tr16(bp), hi = tr16(bp + 4 * stride);
+      if (!from_q && t >= C::VT) {
+        lo = bs4{0, 0, 0, 0};
+        hi = bs4{0, 0, 0, 0};
+      }
+      const bf16x8 bB = __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                          hi[1], hi[2], hi[3]});
+      const f32x4 c = mfma_bf16_16x16x32(aT, bB, f32x4{0.f, 0.f, 0.f, 0.f});
+      // C: column 16t + col, rows 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (jrow[i] >= 0)
+          unsafeAtomicAdd(dkv + ((size_t)b * N + jrow[i]) * DQK + 16 * t + col, c[i]);
+    }
+    __builtin_amdgcn_wave_barrier();  // st and the tile are reused next tile
+  }
+  // dq of this wave's tiles (the waves' partial sums are added atomically)
+  float* dqr = dq + ((size_t)r * Hq + h0 + col) * DQK;
+#pragma unroll
+  for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dqr + 16 * t + 4 * g + i, scale * dqa[t][i]);
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t zero(float* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t stream) {
+  const long long rows = a.B * a.M;
+  const long long blocks = rows * (a.Hq / 16);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipError_t err = zero(a.dq, (size_t)rows * a.Hq * DQK, stream);
+  if (err == hipSuccess) err = zero(a.dkv, (size_t)a.B * a.N * DQK, stream);
+  if (err == hipSuccess && a.dsink) err = zero(a.dsink, (size_t)a.Hq, stream);
+  if (err != hipSuccess) return err;
+  const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)DQK);
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipLaunchKernelGGL((sparse_attn_bwd_kernel<DQK, DV>), dim3((unsigned)blocks),
+                     dim3(BwdCfg<DQK, DV>::THREADS), 0, stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.kv, a.attn_sink, a.topk_idxs, (const uint16_t*)a.o,
+                     (const uint16_t*)a.dO, a.dq, a.dkv, a.dsink, (int)a.M, (int)a.N, a.Hq, a.K,
+                     scale, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_supported(int Hq, int Dqk, int Dv) {
+  if (Hq % 16 != 0 || Hq <= 0 || Hq > 128) return false;
+  return (Dqk == 64 && Dv == 64) || (Dqk == 576 && Dv == 512);
+}
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
+  if (a.Dqk == 64 && a.Dv == 64) return launch_bwd<64, 64>(a, stream);
+  if (a.Dqk == 576 && a.Dv == 512) return launch_bwd<576, 512>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

@@ -6,6 +6,8 @@
  *   2. dsa_topk            -- exact per-row top-k over those scores
  *   3. dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink
  *   4. dsa_prefill         -- 1 -> 2 -> 3 on one stream
+ * and dsa_indexer_topk (1 + 2 without the logits buffer) and
+ * dsa_sparse_attn_bwd (the gradients of 3).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -210,6 +212,39 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
                                int32_t Dv, int32_t K, float sm_scale,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * dsa_sparse_attn_bwd -- gradients of dsa_sparse_attn_fwd (bf16 kv).
+ *
+ * Defined by the TileLang "deepseek_v32" examples page, section "Sparse MLA
+ * Backward" (dP from dO and V, Delta = rowsum(dO * O), dS = P * (dP -
+ * Delta), dQ from dS and K, dKV scattered to the gathered rows with
+ * atomics), applied to the forward above: for each (b, t, h), with p_j the
+ * softmax weight of index j (sink in the denominator) and p_sink the sink's,
+ *   dp_j  = sum_{c<Dv} dO[b,t,h,c] kv[b,j,c]
+ *   Delta = sum_{c<Dv} dO[b,t,h,c] o[b,t,h,c]
+ *   ds_j  = p_j (dp_j - Delta)
+ *   dq[b,t,h,d]  = sm_scale sum_j ds_j kv[b,j,d]                   d < Dqk
+ *   dkv[b,j,d]  += sm_scale ds_j q[b,t,h,d] + (d < Dv ? p_j dO[b,t,h,d] : 0)
+ *   dsink[h]    += -p_sink Delta
+ * summed over every (t, h) and every occurrence of j; invalid indices (-1 or
+ * outside [0, N)) and rows without a valid index contribute nothing.
+ *
+ *   q [B,M,Hq,Dqk], kv [B,N,Dqk], o and dO [B,M,Hq,Dv]: bf16 (o is the
+ *   forward's output for the same inputs); attn_sink [Hq] fp32 or NULL;
+ *   topk_idxs [B,M,K] int32
+ *   dq [B,M,Hq,Dqk], dkv [B,N,Dqk], dsink [Hq] (NULL iff attn_sink is NULL):
+ *   fp32 outputs, overwritten (the call zero-fills them, then accumulates).
+ * Supported: Hq a multiple of 16 up to 128; (Dqk, Dv) in {(64, 64), (576,
+ * 512)}; 1 <= K <= 4096.  P and dS enter the MFMA products rounded to bf16,
+ * everything else is fp32; dkv and dq are accumulated with fp32 atomics, so
+ * their last bits depend on the order the hardware applies them in.
+ */
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const float* attn_sink,
+                               const int32_t* topk_idxs, const void* o, const void* dO,
+                               float* dq, float* dkv, float* dsink, int64_t B, int64_t M,
+                               int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K,
+                               float sm_scale, void* stream);
 
 /*
  * dsa_prefill -- the whole path on one stream: indexer scores into `logits`,

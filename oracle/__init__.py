@@ -47,7 +47,7 @@ def _bind(L):
                                          i32, i32, i32, i32, f64, P, i64, P]
     L.dsa_oracle_sparse_attn_bwd.restype = ctypes.c_int
     L.dsa_oracle_sparse_attn_bwd.argtypes = [P, P, P, P, P, i64, i64, i64, i32, i32, i32,
-                                             i32, f64, P, i64, P, P, P, P, P]
+                                             i32, f64, P, i64, P, P, P, P, P, P]
     L.dsa_oracle_num_threads.restype = ctypes.c_int
     return L
 
@@ -172,7 +172,8 @@ def sparse_attn_bwd(q, kv, attn_sink, topk_idxs, dO, sm_scale, dv, rows=None,
                     with_terms=False):
     """(dq [n_rows, Hq, Dqk], dkv [B, N, Dqk], dsink [Hq] or None), fp64, of
     the bf16 sparse attention; dkv and dsink hold the listed rows'
-    contributions.  with_terms: also (tdq, tdkv), sums of |terms|."""
+    contributions.  with_terms: also (tdq, tdkv, tdsink or None), sums of
+    |terms|."""
     q16 = _np(q, np.uint16)
     B, M, Hq, Dqk = q16.shape
     kvn = _np(kv, np.uint16)
@@ -191,12 +192,13 @@ def sparse_attn_bwd(q, kv, attn_sink, topk_idxs, dO, sm_scale, dv, rows=None,
     dsink = np.empty(Hq, np.float64) if sink is not None else None
     tdq = np.empty_like(dq) if with_terms else None
     tdkv = np.empty_like(dkv) if with_terms else None
+    tds = np.empty(Hq, np.float64) if (with_terms and sink is not None) else None
     rc = lib().dsa_oracle_sparse_attn_bwd(_ptr(q16), _ptr(kvn), _ptr(sink), _ptr(idx),
                                           _ptr(g16), B, M, N, Hq, Dqk, dv, K,
                                           float(sm_scale), _ptr(r), n, _ptr(dq), _ptr(dkv),
-                                          _ptr(dsink), _ptr(tdq), _ptr(tdkv))
+                                          _ptr(dsink), _ptr(tdq), _ptr(tdkv), _ptr(tds))
     if rc != 0:
         raise ValueError("oracle sparse_attn_bwd: invalid argument")
     if with_terms:
-        return dq, dkv, dsink, tdq, tdkv
+        return dq, dkv, dsink, tdq, tdkv, tds
     return dq, dkv, dsink

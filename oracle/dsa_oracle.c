@@ -308,7 +308,8 @@ int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
                                int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
                                int32_t K, double sm_scale, const int64_t* rows,
                                int64_t n_rows, double* dq, double* dkv,
-                               double* dsink, double* tdq, double* tdkv) {
+                               double* dsink, double* tdq, double* tdkv,
+                               double* tdsink) {
   if (!q || !kv || !topk_idxs || !dO || !dq || !dkv) return -1;
   if (sink && !dsink) return -1;
   if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Dqk <= 0 || Dv <= 0 ||
@@ -323,6 +324,8 @@ int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
   }
   if (dsink)
     for (int32_t h = 0; h < Hq; ++h) dsink[h] = 0.0;
+  if (tdsink)
+    for (int32_t h = 0; h < Hq; ++h) tdsink[h] = 0.0;
   int failed = 0;
 
 #pragma omp parallel
@@ -375,26 +378,43 @@ int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
         /* Delta = sum_j p_j dp_j */
         double delta = 0.0;
         for (int32_t j = 0; j < nj; ++j) delta += exp(sc[j] - mx) / den * dp[j];
+        /* for the |term| sums: sum_c |dO[c]| |o[c]|, the terms of Delta
+         * written as dO . o */
+        double dabs = 0.0;
+        if (tg || tdkv || tdsink) {
+          for (int32_t c = 0; c < Dv; ++c) {
+            double oc = 0.0;
+            for (int32_t j = 0; j < nj; ++j)
+              oc += exp(sc[j] - mx) / den *
+                    dsa_oracle_bf16_value(kv[(b * N + J[j]) * (int64_t)Dqk + c]);
+            dabs += fabs(gv[c]) * fabs(oc);
+          }
+        }
         if (sink) {
           double ps = exp(sk - mx) / den;
 #pragma omp atomic
           dsink[h] += -ps * delta;
+          if (tdsink) {
+#pragma omp atomic
+            tdsink[h] += ps * dabs;
+          }
         }
         for (int32_t j = 0; j < nj; ++j) {
           double p = exp(sc[j] - mx) / den;
           double ds = p * (dp[j] - delta);
+          double dsabs = p * (fabs(dp[j]) + dabs); /* |terms| of ds */
           const uint16_t* kr = kv + (b * N + J[j]) * (int64_t)Dqk;
           double* gk = dkv + (b * N + J[j]) * (int64_t)Dqk;
           double* tk = tdkv ? tdkv + (b * N + J[j]) * (int64_t)Dqk : NULL;
           for (int32_t d = 0; d < Dqk; ++d) {
             double kvd = dsa_oracle_bf16_value(kr[d]);
             g[d] += sm_scale * ds * kvd;
-            if (tg) tg[d] += sm_scale * fabs(ds) * fabs(kvd);
+            if (tg) tg[d] += sm_scale * dsabs * fabs(kvd);
             double add = sm_scale * ds * qv[d] + (d < Dv ? p * gv[d] : 0.0);
 #pragma omp atomic
             gk[d] += add;
             if (tk) {
-              double tadd = sm_scale * fabs(ds) * fabs(qv[d]) + (d < Dv ? p * fabs(gv[d]) : 0.0);
+              double tadd = sm_scale * dsabs * fabs(qv[d]) + (d < Dv ? p * fabs(gv[d]) : 0.0);
 #pragma omp atomic
               tk[d] += tadd;
             }

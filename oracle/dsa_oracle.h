@@ -101,15 +101,19 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
  *   dkv   [B, N, Dqk] fp64: the listed rows' contributions (overwritten)
  *   dsink [Hq] fp64 (listed rows), or NULL when sink is NULL
  *   tdq, tdkv: NULL, or the same shapes holding the sums of the absolute
- *   values of the terms above (sm_scale |ds_j| |kv_j[d]|, and sm_scale
- *   |ds_j| |q[d]| + p_j |dO[d]|), for tolerances.                          */
+ *   values of the terms above, with ds_j expanded into its terms p_j dp_j
+ *   and p_j dO[c] o[c] (c < Dv): with A_j = p_j (|dp_j| + sum_c |dO[c]|
+ *   |o[c]|), sm_scale A_j |kv_j[d]|, and sm_scale A_j |q[d]| + p_j |dO[d]|;
+ *   tdsink: NULL, or [Hq] with sum p_sink sum_c |dO[c]| |o[c]|; for
+ *   tolerances.                                                            */
 int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,
                                const float* sink, const int32_t* topk_idxs,
                                const uint16_t* dO, int64_t B, int64_t M,
                                int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
                                int32_t K, double sm_scale, const int64_t* rows,
                                int64_t n_rows, double* dq, double* dkv,
-                               double* dsink, double* tdq, double* tdkv);
+                               double* dsink, double* tdq, double* tdkv,
+                               double* tdsink);
 
 /* Number of OpenMP threads the oracle runs with (0 if built without). */
 int dsa_oracle_num_threads(void);

@@ -583,6 +583,14 @@ def check_attn_bwd_closed_forms(seed=42):
     b_ = oracle.sparse_attn_bwd(qb, kvb, sink, idx3, gb, 0.5, Dv)
     for x, y in zip(a, b_):
         assert np.array_equal(x, y)
+    # the |term| sums bound the gradients (triangle inequality) and vanish
+    # with them
+    _, _, _, tq, tk, ts = oracle.sparse_attn_bwd(qb, kvb, sink, idx2, gb, 0.5, Dv,
+                                                 with_terms=True)
+    assert np.all(tq >= np.abs(a[0]) * (1 - 1e-12)) and np.all(tk >= np.abs(a[1]) * (1 - 1e-12))
+    assert np.all(ts >= np.abs(a[2]) * (1 - 1e-12)) and ts.max() > 0
+    assert tq.max() > 0 and tk.max() > 0
+    assert np.all(tk[0, 2] == 0.0)  # row 2 is gathered by no token
     # rows=[1] equals the full call with row 0's dO set to zero
     r1 = oracle.sparse_attn_bwd(qb, kvb, sink, idx2, gb, 0.5, Dv, rows=[1])
     g0 = gb.copy()
