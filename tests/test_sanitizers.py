@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TESTS = os.path.join(ROOT, "tests")
 ORACLE_SRC = os.path.join(ROOT, "oracle", "dsa_oracle.c")
 CSRC = os.path.join(ROOT, "fp8_indexer_amd", "csrc")
-SOURCES = ("api.hip", "indexer.hip", "topk.hip", "sparse_attn.hip")
+from fp8_indexer_amd.build import SOURCES  # noqa: E402
 ENV_BASE = {"ASAN_OPTIONS": "detect_leaks=0:abort_on_error=0",
             "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1"}
 
