@@ -10,9 +10,12 @@ Prints ONE JSON line.  `value` is tokens/s of the whole step.  `roofline`
 describes the dominant kernel (sparse attention): algorithmic bf16 flops per
 launch over its median duration from HIP events on the launch stream,
 against the 2.5 PFLOP/s dense bf16 MFMA peak.  `stages` also gives each
-stage timed with L2 and the MALL flushed before every step, and the
-dsa_prefill entry point warm and flushed.  `cpu_baseline` times the CPU
-oracle (indexer -> top-k -> attention) on a bounded sample of rows.
+stage timed with L2 and the MALL flushed before every step, the dsa_prefill
+entry point warm and flushed, the indexer + top-k without a logits buffer
+(dsa_indexer_topk: time, and peak device memory against the unfused way),
+and the attention backward at the same shapes (bf16 kv).  `cpu_baseline`
+times the CPU oracle (indexer -> top-k -> attention), stage by stage, on a
+bounded sample of rows.
 
     python bench.py [--steps 20] [--warmup 5] [--gpus 1] [--no-cpu] [--flush-reps 10]
     python bench.py --copy-calibration     # plain 1 GiB copy, for counter scaling
@@ -77,9 +80,23 @@ def load_traffic(launches_per_step=1):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, x, budget_s):
-    """The oracle on a bounded sample of rows, evenly spaced over the
-    sequence so that the average window length matches the workload."""
+    """The oracle (indexer -> top-k -> attention) on a bounded sample of
+    rows, evenly spaced over the sequence so that the window lengths span
+    the workload's; each stage timed on its own, with its algorithmic work
+    over the sampled rows."""
     import numpy as np
     import oracle
     R = wl.B * wl.M
@@ -88,25 +105,41 @@ def cpu_baseline(wl, x, budget_s):
         t0 = time.perf_counter()
         lg = oracle.indexer_logits(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"],
                                    x["ks"], x["ke"], rows=rows)
+        t1 = time.perf_counter()
         ti = oracle.topk(lg, x["ks"], x["ke"], wl.B, wl.M, wl.N, wl.K, rows=rows)
+        t2 = time.perf_counter()
         full = np.full((R, wl.K), -1, np.int32)
         full[rows] = ti
         oracle.sparse_attn(x["q"], x["kv"], x["sink"], full.reshape(wl.B, wl.M, wl.K),
                            wl.sm_scale, wl.Dv, kv_scale=x["kv_scale"], rows=rows)
-        return time.perf_counter() - t0
+        t3 = time.perf_counter()
+        return t1 - t0, t2 - t1, t3 - t2
 
     n = 16
     rows = np.linspace(0, R - 1, n).round().astype(np.int64)
-    dt = run(rows)
+    dt = sum(run(rows))
     n2 = int(min(R, max(n, n * (budget_s / max(dt, 1e-3)))))
     if n2 > n:
         rows = np.unique(np.linspace(0, R - 1, n2).round().astype(np.int64))
-        dt = run(rows)
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    t_idx, t_topk, t_att = run(rows)
+    s = np.clip(x["ks"].reshape(-1)[rows].astype(np.int64), 0, wl.N)
+    e = np.maximum(np.clip(x["ke"].reshape(-1)[rows].astype(np.int64), 0, wl.N), s)
+    ln = e - s
+    idx_flops = 2.0 * wl.H * wl.D * ln.sum()
+    topk_bytes = 4.0 * ln[ln > wl.K].sum() + 4.0 * wl.K * len(rows)
+    att_flops = 2.0 * wl.Hq * (wl.Dqk + wl.Dv) * np.minimum(ln, wl.K).sum()
+    total = t_idx + t_topk + t_att
+    return {"value": len(rows) / total, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{len(rows)} of {R} query rows, evenly spaced over the {wl.name} "
-                      f"workload (indexer -> top-k -> attention, fp64 C oracle), "
-                      f"{dt:.1f} s"}
+                      f"workload (indexer -> top-k -> attention, fp64 C oracle, OpenMP), "
+                      f"{total:.1f} s",
+            "stages": {
+                "indexer": {"s": t_idx, "gflops": idx_flops / t_idx / 1e9},
+                "topk": {"s": t_topk, "gbs": topk_bytes / t_topk / 1e9},
+                "attention": {"s": t_att, "gflops": att_flops / t_att / 1e9},
+            }}
 
 
 def copy_calibration():
@@ -132,6 +165,8 @@ def main():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="steps timed with L2/MALL flushed before each (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward-reps", type=int, default=3,
+                    help="timed calls of the attention backward (0 = skip)")
     ap.add_argument("--workload", default="prefill_4096",
                     help="workload to time (default: the 4096-token causal prefill)")
     args = ap.parse_args()
@@ -247,6 +282,74 @@ def main():
     torch.cuda.synchronize()
     ms_prefill = (time.perf_counter() - tp0) * 1e3 / args.steps
 
+    # indexer + top-k without the [B, M, N] logits buffer (dsa_indexer_topk):
+    # time, and peak device memory of either way of producing topk_idxs from
+    # the inputs (logits buffer, or workspace)
+    eprint("[bench] fused indexer + top-k")
+    fused_idx = torch.empty_like(idx)
+
+    def fused_step():
+        dsa.indexer_topk(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"], g["ke"],
+                         wl.K, out=fused_idx)
+
+    for _ in range(2):
+        fused_step()
+    torch.cuda.synchronize()
+    fev = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fused_step()
+        e1.record(stream)
+        fev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms_fused = float(np.median([a.elapsed_time(b) for a, b in fev]))
+    fused_same = bool(torch.equal(fused_idx, idx))
+
+    def peak_bytes(fn):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() - base
+
+    del logits
+    torch.cuda.empty_cache()
+    peak_unfused = peak_bytes(lambda: dsa.topk(
+        dsa.indexer_logits(g["q8"], g["q_scale"], g["k8"], g["k_scale"], g["w"], g["ks"],
+                           g["ke"]), g["ks"], g["ke"], wl.K, out=fused_idx))
+    peak_fused = peak_bytes(fused_step)
+
+    # backward of the sparse attention at the same shapes (bf16 kv only)
+    bwd = None
+    if not wl.kv_fp8 and args.backward_reps > 0:
+        eprint("[bench] backward")
+        gO = torch.randn(o.shape, device=dev).to(torch.bfloat16)
+        dq = torch.empty((B, M, wl.Hq, wl.Dqk), dtype=torch.float32, device=dev)
+        dkv = torch.empty((B, N, wl.Dqk), dtype=torch.float32, device=dev)
+        dsk = torch.empty((wl.Hq,), dtype=torch.float32, device=dev)
+        bargs = (g["q"], g["kv"], g["sink"], idx, o, gO, wl.sm_scale, dq, dkv, dsk)
+        dsa.sparse_attn_bwd(*bargs)
+        torch.cuda.synchronize()
+        bt = []
+        for _ in range(args.backward_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsa.sparse_attn_bwd(*bargs)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bt.append(e0.elapsed_time(e1))
+        ms_bwd = float(np.median(bt))
+        # S and dP (recomputed), dQ, dK and dV products per valid index
+        bwd_flops = 2.0 * wl.Hq * (3 * wl.Dqk + 2 * wl.Dv) * work_counts(wl, x["ks"],
+                                                                          x["ke"])["p_att"]
+        bwd = {"ms": ms_bwd, "tflops": bwd_flops / (ms_bwd * 1e-3) / 1e12,
+               "frac_bf16_peak": bwd_flops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "algorithmic_tflop": bwd_flops / 1e12, "reps": args.backward_reps}
+        del dq, dkv, gO
+
     wc = work_counts(wl, x["ks"], x["ke"])
     tokens = B * M
     att_tflops = wc["att_flops"] / (ms_att * 1e-3) / 1e12
@@ -292,6 +395,11 @@ def main():
                        "a second run of as many steps with events at every stage boundary"),
             "e2e_roofline_ms": roof_s * 1e3,
             "e2e_frac_of_roofline": roof_s * 1e3 / ms_step,
+            "indexer_topk_fused": {
+                "ms": ms_fused, "same_topk_as_unfused": fused_same,
+                "peak_bytes": peak_fused, "unfused_peak_bytes": peak_unfused,
+                "logits_buffer_bytes": B * M * N * 4},
+            "backward": bwd,
         },
         "cpu_baseline": None,
     }
