@@ -300,8 +300,36 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   __shared__ int sWave[kTkWaves];
   __shared__ int sCnt[2][kTkWaves];
   __shared__ int sSel[3];
-  for (int r = blockIdx.x; r < rows; r += gridDim.x)
-    topk_stream_row(logits, ks, ke, out, N, K, skip_len, (size_t)r, hist, sWave, sCnt, sSel);
+  __shared__ int sRows[kTkThreads];
+  __shared__ int sNum;
+  if (skip_len <= 0) {
+    for (int r = blockIdx.x; r < rows; r += gridDim.x)
+      topk_stream_row(logits, ks, ke, out, N, K, 0, (size_t)r, hist, sWave, sCnt, sSel);
+    return;
+  }
+  // Only rows longer than skip_len are this launch's.  Workgroup g owns rows
+  // g, g + G, g + 2G, ...: each thread tests one of up to kTkThreads of them
+  // at a time, the long ones are listed in LDS, and the workgroup then runs
+  // them one by one.
+  const long long G = gridDim.x;
+  for (long long k0 = 0; k0 * G < rows; k0 += kTkThreads) {
+    const long long rr = blockIdx.x + (k0 + threadIdx.x) * G;
+    const int r = rr < rows ? (int)rr : rows;
+    bool lng = false;
+    if (r < rows) {
+      const int s = clampi(ks[r], 0, N);
+      lng = clampi(ke[r], s, N) - s > skip_len;
+    }
+    if (threadIdx.x == 0) sNum = 0;
+    __syncthreads();
+    if (lng) sRows[atomicAdd(&sNum, 1)] = r;  // order does not matter
+    __syncthreads();
+    const int n = sNum;
+    for (int i = 0; i < n; ++i)
+      topk_stream_row(logits, ks, ke, out, N, K, skip_len, (size_t)sRows[i], hist, sWave, sCnt,
+                      sSel);
+    __syncthreads();  // sRows and sNum are rewritten next
+  }
 }
 
 // ---- four waves per row ----------------------------------------------------
