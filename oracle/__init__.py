@@ -45,6 +45,9 @@ def _bind(L):
     L.dsa_oracle_sparse_attn.restype = ctypes.c_int
     L.dsa_oracle_sparse_attn.argtypes = [P, P, i32, P, P, P, i64, i64, i64,
                                          i32, i32, i32, i32, f64, P, i64, P]
+    L.dsa_oracle_sparse_attn_ex.restype = ctypes.c_int
+    L.dsa_oracle_sparse_attn_ex.argtypes = [P, i32, P, P, i32, P, P, P, i64, i64, i64,
+                                            i32, i32, i32, i32, f64, P, i64, P, P]
     L.dsa_oracle_sparse_attn_bwd.restype = ctypes.c_int
     L.dsa_oracle_sparse_attn_bwd.argtypes = [P, P, P, P, P, i64, i64, i64, i32, i32, i32,
                                              i32, f64, P, i64, P, P, P, P, P, P]
@@ -72,6 +75,14 @@ def _np(x, dtype):
         else:
             x = x.astype(dtype)
     return x
+
+
+def _is_fp8(x):
+    """True for e4m3fn codes: a torch float8_e4m3fn tensor or 8-bit integers."""
+    if hasattr(x, "detach"):
+        import torch
+        return x.dtype in (torch.float8_e4m3fn, torch.uint8, torch.int8)
+    return np.asarray(x).dtype.itemsize == 1
 
 
 def _ptr(a):
@@ -143,11 +154,18 @@ def topk(logits_rows, ks, ke, B, M, N, K, rows=None):
     return out
 
 
-def sparse_attn(q, kv, attn_sink, topk_idxs, sm_scale, dv, kv_scale=None, rows=None):
-    """o [n_rows, Hq, Dv] fp64.  q [B,M,Hq,Dqk] bf16; kv [B,N,Dqk] bf16, or
-    e4m3fn codes with kv_scale [B,N]."""
-    q16 = _np(q, np.uint16)
-    B, M, Hq, Dqk = q16.shape
+def sparse_attn(q, kv, attn_sink, topk_idxs, sm_scale, dv, kv_scale=None, rows=None,
+                q_scale=None, q_fp8=None, with_terms=False):
+    """o [n_rows, Hq, Dv] fp64.  q [B,M,Hq,Dqk]: bf16, or e4m3fn codes (uint8
+    or torch float8_e4m3fn; q_fp8 may say so explicitly) with q_scale
+    [B,M,Hq] (None = 1); kv [B,N,Dqk] bf16, or e4m3fn codes with kv_scale
+    [B,N].  with_terms: (o, terms), terms[..., c] = sum_j p_j |v_jc|."""
+    if q_fp8 is None:
+        q_fp8 = _is_fp8(q)
+    if q_scale is not None and not q_fp8:
+        raise ValueError("oracle sparse_attn: q_scale needs an fp8 q")
+    qn = _np(q, np.uint8 if q_fp8 else np.uint16)
+    B, M, Hq, Dqk = qn.shape
     fp8 = kv_scale is not None
     kvn = _np(kv, np.uint8 if fp8 else np.uint16)
     N = kvn.shape[1]
@@ -157,15 +175,20 @@ def sparse_attn(q, kv, attn_sink, topk_idxs, sm_scale, dv, kv_scale=None, rows=N
     assert idx.size == B * M * K
     sink = _np(attn_sink, np.float32)
     kvs = _np(kv_scale, np.float32)
+    qs = _np(q_scale, np.float32)
+    if qs is not None:
+        assert qs.size == B * M * Hq
     r, n = _rows(rows)
     n_out = n if r is not None else B * M
     out = np.empty((n_out, Hq, dv), np.float64)
-    rc = lib().dsa_oracle_sparse_attn(_ptr(q16), _ptr(kvn), int(fp8), _ptr(kvs),
-                                      _ptr(sink), _ptr(idx), B, M, N, Hq, Dqk, dv,
-                                      K, float(sm_scale), _ptr(r), n, _ptr(out))
+    terms = np.empty((n_out, Hq, dv), np.float64) if with_terms else None
+    rc = lib().dsa_oracle_sparse_attn_ex(_ptr(qn), int(bool(q_fp8)), _ptr(qs), _ptr(kvn),
+                                         int(fp8), _ptr(kvs), _ptr(sink), _ptr(idx), B, M,
+                                         N, Hq, Dqk, dv, K, float(sm_scale), _ptr(r), n,
+                                         _ptr(out), _ptr(terms))
     if rc != 0:
         raise ValueError("oracle sparse_attn: invalid argument")
-    return out
+    return (out, terms) if with_terms else out
 
 
 def sparse_attn_bwd(q, kv, attn_sink, topk_idxs, dO, sm_scale, dv, rows=None,

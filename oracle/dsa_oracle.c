@@ -214,13 +214,15 @@ int dsa_oracle_topk(const float* logits, const int32_t* ks, const int32_t* ke,
 /* Sparse attention with sink                                                */
 /* ------------------------------------------------------------------------ */
 
-int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
-                           const float* kv_scale, const float* sink,
-                           const int32_t* topk_idxs, int64_t B, int64_t M,
-                           int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
-                           int32_t K, double sm_scale, const int64_t* rows,
-                           int64_t n_rows, double* o) {
+int dsa_oracle_sparse_attn_ex(const void* q, int32_t q_fp8, const float* q_scale,
+                              const void* kv, int32_t kv_fp8,
+                              const float* kv_scale, const float* sink,
+                              const int32_t* topk_idxs, int64_t B, int64_t M,
+                              int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
+                              int32_t K, double sm_scale, const int64_t* rows,
+                              int64_t n_rows, double* o, double* terms) {
   if (!q || !kv || !topk_idxs || !o) return -1;
+  if (!q_fp8 && q_scale) return -1;
   if (kv_fp8 && !kv_scale) return -1;
   if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Dqk <= 0 || Dv <= 0 ||
       Dv > Dqk || K <= 0)
@@ -265,10 +267,21 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
       }
       for (int32_t h = 0; h < Hq; ++h) {
         double* oh = o + (i * Hq + h) * (int64_t)Dv;
+        double* th = terms ? terms + (i * Hq + h) * (int64_t)Dv : NULL;
         for (int32_t c = 0; c < Dv; ++c) oh[c] = 0.0;
+        if (th)
+          for (int32_t c = 0; c < Dv; ++c) th[c] = 0.0;
         if (nj == 0) continue; /* all-invalid row: zero output */
-        const uint16_t* qh = q + (r * Hq + h) * (int64_t)Dqk;
-        for (int32_t d = 0; d < Dqk; ++d) qv[d] = dsa_oracle_bf16_value(qh[d]);
+        const int64_t qoff = (r * Hq + h) * (int64_t)Dqk;
+        if (q_fp8) {
+          /* fp8 query: decoded code times the (token, head) scale */
+          const double qsc = q_scale ? (double)q_scale[r * Hq + h] : 1.0;
+          for (int32_t d = 0; d < Dqk; ++d)
+            qv[d] = dsa_oracle_e4m3fn_value(((const uint8_t*)q)[qoff + d]) * qsc;
+        } else {
+          for (int32_t d = 0; d < Dqk; ++d)
+            qv[d] = dsa_oracle_bf16_value(((const uint16_t*)q)[qoff + d]);
+        }
         double mx = -INFINITY;
         for (int32_t j = 0; j < nj; ++j) {
           double acc = 0.0;
@@ -285,9 +298,13 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
           den += p;
           const double* vr = rowv + (int64_t)j * Dqk;
           for (int32_t c = 0; c < Dv; ++c) oh[c] += p * vr[c];
+          if (th)
+            for (int32_t c = 0; c < Dv; ++c) th[c] += p * fabs(vr[c]);
         }
         if (sink) den += exp(sk - mx);
         for (int32_t c = 0; c < Dv; ++c) oh[c] /= den;
+        if (th)
+          for (int32_t c = 0; c < Dv; ++c) th[c] /= den;
       }
     }
     free(rowv);
@@ -300,6 +317,16 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
 
 /* ------------------------------------------------------------------------ */
 /* Sparse attention backward                                                 */
+int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
+                           const float* kv_scale, const float* sink,
+                           const int32_t* topk_idxs, int64_t B, int64_t M,
+                           int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
+                           int32_t K, double sm_scale, const int64_t* rows,
+                           int64_t n_rows, double* o) {
+  return dsa_oracle_sparse_attn_ex(q, 0, NULL, kv, kv_fp8, kv_scale, sink, topk_idxs, B, M,
+                                   N, Hq, Dqk, Dv, K, sm_scale, rows, n_rows, o, NULL);
+}
+
 /* ------------------------------------------------------------------------ */
 
 int dsa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* kv,

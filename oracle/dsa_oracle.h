@@ -84,6 +84,25 @@ int dsa_oracle_sparse_attn(const uint16_t* q, const void* kv, int32_t kv_fp8,
                            int32_t K, double sm_scale, const int64_t* rows,
                            int64_t n_rows, double* o);
 
+/* The same attention with the query optionally in fp8 (full-FP8 attention:
+ * TileLang "deepseek_v32" page, section "Sparse MLA Forward (FP8)", an e4m3
+ * query and KV cache with a bf16 output).  q_fp8 = 0: q holds bf16 bits and
+ * q_scale must be NULL; q_fp8 = 1: q holds e4m3fn codes and the query value
+ * is code_value * q_scale[b,t,h] (q_scale [B,M,Hq] fp32, NULL = 1).  The
+ * result is the exact attention of those values: the fp8 rounding of the
+ * probabilities that the GPU path applies is not modelled here (it is the
+ * GPU path's rounding, bounded through `terms`).
+ * terms (NULL or [n_rows, Hq, Dv] fp64): terms[c] = sum_j exp(s_j - Mx) *
+ * |kv_value[b,j,c]| / den, the magnitude of what each output element sums
+ * (equal to o[c] when every value is >= 0).                                 */
+int dsa_oracle_sparse_attn_ex(const void* q, int32_t q_fp8, const float* q_scale,
+                              const void* kv, int32_t kv_fp8,
+                              const float* kv_scale, const float* sink,
+                              const int32_t* topk_idxs, int64_t B, int64_t M,
+                              int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv,
+                              int32_t K, double sm_scale, const int64_t* rows,
+                              int64_t n_rows, double* o, double* terms);
+
 /* Gradients of that sparse attention (TileLang deepseek_v32 page, "Sparse
  * MLA Backward": dP from dO and V, Delta = rowsum(dO * O), dS = P * (dP -
  * Delta), dQ from dS and K, dKV scattered back to the gathered rows).  For

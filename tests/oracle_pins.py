@@ -300,9 +300,10 @@ def _bf16_bits(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
 
 
-def _attn_dense(qv, kvv, sink, idx, sm_scale, dv):
+def _attn_dense(qv, kvv, sink, idx, sm_scale, dv, vals=None):
     """Textbook softmax over ALL N keys plus one sink column with a zero value
-    row; keys not in idx are masked with weight 0 (idx without duplicates)."""
+    row; keys not in idx are masked with weight 0 (idx without duplicates).
+    vals: the value rows (default: the first dv columns of kvv)."""
     B, M, Hq, Dqk = qv.shape
     N = kvv.shape[1]
     out = np.zeros((B * M, Hq, dv))
@@ -321,8 +322,9 @@ def _attn_dense(qv, kvv, sink, idx, sm_scale, dv):
                 mx = cols[wts > 0].max()
                 ex = wts * np.exp(cols - mx)
                 p = ex / ex.sum()
-                vals = np.concatenate([kvv[b][:, :dv], np.zeros((1, dv))])  # sink value row 0
-                out[b * M + t, h] = p @ vals
+                vb = (kvv if vals is None else vals)[b][:, :dv]
+                vrows = np.concatenate([vb, np.zeros((1, dv))])  # sink value row 0
+                out[b * M + t, h] = p @ vrows
     return out
 
 
@@ -436,6 +438,70 @@ def check_attn_fp8_kv(seed=24):
     qd = _torch_bf16(qb.view(np.uint16).ravel()).reshape(qb.shape)
     ref = _attn_dense(qd, kvv, sink, idx, 0.4, 6)
     assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def check_attn_fp8_q(seed=25):
+    """fp8 query (the full-FP8 attention's input): the query value is
+    decode(code) * q_scale[b,t,h].  With power-of-two scales those values are
+    exact in bf16, so the result must equal the bf16-query path fed with
+    them; with any scale it must equal the dense formula on torch-decoded
+    values; a scale common to every (t, h) is the same as folding it into
+    sm_scale."""
+    rng = np.random.default_rng(seed)
+    B, M, N, Hq, Dqk, K = 1, 3, 9, 3, 8, 5
+    q8 = _rand_e4m3(rng, (B, M, Hq, Dqk))
+    qs = np.float32(2.0) ** rng.integers(-3, 4, (B, M, Hq)).astype(np.float32)
+    kvv = rng.standard_normal((B, N, Dqk)).astype(np.float32)
+    kvb = _bf16_bits(kvv)
+    idx = np.int32(np.stack([rng.permutation(N)[:K] for _ in range(B * M)]).reshape(B, M, K))
+    idx[0, 1, 2:] = -1
+    idx[0, 2, :] = -1
+    sink = rng.standard_normal(Hq).astype(np.float32)
+    got = oracle.sparse_attn(q8, kvb, sink, idx, 0.4, 6, q_scale=qs)
+    qd = _torch_e4m3(q8.ravel()).reshape(q8.shape) * qs[..., None].astype(np.float64)
+    same = oracle.sparse_attn(_bf16_bits(qd.astype(np.float32)), kvb, sink, idx, 0.4, 6)
+    assert np.allclose(got, same, rtol=1e-14, atol=1e-16)
+    kd = _torch_bf16(kvb.view(np.uint16).ravel()).reshape(kvb.shape)
+    ref = _attn_dense(qd, kd, sink, idx, 0.4, 6)
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+    assert not got[2].any()
+    # no scale = scale 1; a common non-power-of-two scale folds into sm_scale
+    one = oracle.sparse_attn(q8, kvb, sink, idx, 0.4, 6)
+    assert np.array_equal(one, oracle.sparse_attn(q8, kvb, sink, idx, 0.4, 6,
+                                                  q_scale=np.ones((B, M, Hq), np.float32)))
+    a = np.float32(0.37)
+    sc = oracle.sparse_attn(q8, kvb, sink, idx, 0.4, 6, q_scale=np.full((B, M, Hq), a))
+    assert np.allclose(sc, oracle.sparse_attn(q8, kvb, sink, idx, 0.4 * float(a), 6),
+                       rtol=1e-12, atol=1e-15)
+    # fp8 query and fp8 KV together
+    kv8 = _rand_e4m3(rng, (B, N, Dqk))
+    ks = rng.uniform(0.01, 0.1, (B, N)).astype(np.float32)
+    got = oracle.sparse_attn(q8, kv8, sink, idx, 0.4, 6, kv_scale=ks, q_scale=qs)
+    kvd = _torch_e4m3(kv8.ravel()).reshape(kv8.shape) * ks[..., None].astype(np.float64)
+    ref = _attn_dense(qd, kvd, sink, idx, 0.4, 6)
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def check_attn_terms(seed=26):
+    """The per-element term sums sum_j p_j |v_jc| that bound the GPU path's
+    rounding: the dense formula on |v|, equal to o when every value is >= 0,
+    never below |o|, zero for rows without a valid index."""
+    rng = np.random.default_rng(seed)
+    qb, kvb, idx, sink = _rand_attn(rng, dup=True)
+    o, t = oracle.sparse_attn(qb, kvb, sink, idx, 0.3, 8, with_terms=True)
+    assert np.array_equal(o, oracle.sparse_attn(qb, kvb, sink, idx, 0.3, 8))
+    assert (t >= np.abs(o) * (1 - 1e-12)).all()
+    qd = _torch_bf16(qb.view(np.uint16).ravel()).reshape(qb.shape)
+    kd = _torch_bf16(kvb.view(np.uint16).ravel()).reshape(kvb.shape)
+    nodup = _rand_attn(np.random.default_rng(seed + 1))[2]
+    _, t2 = oracle.sparse_attn(qb, kvb, sink, nodup, 0.3, 7, with_terms=True)
+    assert np.allclose(t2, _attn_dense(qd, kd, sink, nodup, 0.3, 7, vals=np.abs(kd)),
+                       rtol=1e-11, atol=1e-13)
+    kpos = _bf16_bits(np.abs(kd).astype(np.float32))
+    o3, t3 = oracle.sparse_attn(qb, kpos, sink, idx, 0.3, 8, with_terms=True)
+    assert np.allclose(o3, t3, rtol=1e-13, atol=1e-15)
+    empty = ~(idx >= 0).any(-1).reshape(-1)
+    assert empty.any() and not t[empty].any()
 
 
 # ------------------------------------------------ row subsets (rows=...) --
@@ -606,6 +672,6 @@ ALL_CHECKS = [
     check_indexer_hand, check_indexer_exact, check_indexer_invariants, check_indexer_terms,
     check_topk_hand, check_topk_bruteforce, check_topk_invariants,
     check_attn_hand, check_attn_dense, check_attn_closed_forms, check_attn_invariants,
-    check_attn_fp8_kv, check_rows_subsets,
+    check_attn_fp8_kv, check_attn_fp8_q, check_attn_terms, check_rows_subsets,
     check_attn_bwd_finite_differences, check_attn_bwd_closed_forms,
 ]

@@ -47,6 +47,12 @@ MUTANTS = [
      "const uint8_t* qr = q + (i * H + h) * D;"),
     ("attn_rows_indices", "const int32_t* idx = topk_idxs + r * K;\n      int32_t nj = 0;\n      for (int32_t j = 0; j < K; ++j)\n        if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      /* decode",
      "const int32_t* idx = topk_idxs + i * K;\n      int32_t nj = 0;\n      for (int32_t j = 0; j < K; ++j)\n        if (idx[j] >= 0 && idx[j] < N) J[nj++] = idx[j];\n      /* decode"),
+    # fp8 query and the term sums
+    ("q8_scale_ignored", "const double qsc = q_scale ? (double)q_scale[r * Hq + h] : 1.0;",
+     "const double qsc = 1.0;"),
+    ("q8_scale_wrong_head", "(double)q_scale[r * Hq + h] : 1.0;", "(double)q_scale[r * Hq] : 1.0;"),
+    ("terms_signed", "th[c] += p * fabs(vr[c]);", "th[c] += p * vr[c];"),
+    ("terms_unnormalised", "for (int32_t c = 0; c < Dv; ++c) th[c] /= den;", ";"),
     # backward
     ("bwd_delta_dropped", "double ds = p * (dp[j] - delta);", "double ds = p * dp[j];"),
     ("bwd_dq_unscaled", "g[d] += sm_scale * ds * kvd;", "g[d] += ds * kvd;"),
