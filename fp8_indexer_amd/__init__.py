@@ -27,7 +27,8 @@ import torch
 __all__ = ["DSAError", "lib", "version", "indexer_logits", "indexer_topk",
            "indexer_topk_workspace_size", "topk", "sparse_attn_fwd", "sparse_attn_bwd",
            "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
-           "prefill_workspace_size", "prefill_noalloc", "KV_BF16", "KV_FP8_E4M3FN",
+           "prefill_workspace_size", "prefill_noalloc", "sparse_attn_fwd_fp8",
+           "sparse_attn_fp8_workspace_size", "KV_BF16", "KV_FP8_E4M3FN",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -35,7 +36,8 @@ KV_BF16, KV_FP8_E4M3FN = 0, 1
 EXPORTS = ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_indexer_topk_workspace_size",
            "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_workspace_size", "dsa_prefill", "dsa_prefill_workspace_size",
-           "dsa_prefill_noalloc", "dsa_sparse_attn_bwd", "dsa_status_string", "dsa_version")
+           "dsa_prefill_noalloc", "dsa_sparse_attn_bwd", "dsa_sparse_attn_fwd_fp8",
+           "dsa_sparse_attn_fp8_workspace_size", "dsa_status_string", "dsa_version")
 NOALLOC_SCRATCH_BYTES = 48 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -91,6 +93,11 @@ def lib():
         L.dsa_sparse_attn_fwd.restype = ctypes.c_int
         L.dsa_sparse_attn_fwd.argtypes = [P, P, ctypes.c_int, P, P, P, P, i64, i64, i64, i32,
                                           i32, i32, i32, ctypes.c_float, P, sz, P]
+        L.dsa_sparse_attn_fp8_workspace_size.restype = ctypes.c_int
+        L.dsa_sparse_attn_fp8_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, psz]
+        L.dsa_sparse_attn_fwd_fp8.restype = ctypes.c_int
+        L.dsa_sparse_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32,
+                                              i32, ctypes.c_float, P, sz, P]
         L.dsa_sparse_attn_bwd.restype = ctypes.c_int
         L.dsa_sparse_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32,
                                           i32, i32, ctypes.c_float, P]
@@ -194,6 +201,15 @@ def sparse_attn_workspace_size(B, M, Hq, Dqk, Dv, K):
     return n.value
 
 
+def sparse_attn_fp8_workspace_size(B, M, Hq, Dqk, Dv, K):
+    """Bytes of scratch dsa_sparse_attn_fwd_fp8's fastest path needs on the
+    current device (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check("dsa_sparse_attn_fp8_workspace_size",
+           lib().dsa_sparse_attn_fp8_workspace_size(B, M, Hq, Dqk, Dv, K, ctypes.byref(n)))
+    return n.value
+
+
 def indexer_logits(q, q_scale, k, k_scale, weights, ks, ke, logits=None):
     """logits [B,M,N] fp32 (entries outside each row's window are untouched)."""
     B, M, H, D = _rank(q, "q", 4)
@@ -291,6 +307,37 @@ def sparse_attn_fwd(q, kv, attn_sink, topk_idxs, sm_scale=0.0, dv=None, kv_scale
             _ptr(q), _ptr(kv), KV_FP8_E4M3FN if fp8 else KV_BF16, _ptr(kv_scale),
             _ptr(attn_sink), _ptr(topk_idxs), _ptr(out), B, M, N, Hq, Dqk, dv, K,
             float(sm_scale), wp, wn, _stream(q)))
+    return out
+
+
+def sparse_attn_fwd_fp8(q, q_scale, kv, kv_scale, attn_sink, topk_idxs, sm_scale=0.0, dv=512,
+                        out=None, workspace="auto"):
+    """o [B,M,Hq,Dv] bf16 of the full-FP8 attention: q [B,M,Hq,Dqk] and kv
+    [B,N,Dqk] e4m3fn codes with q_scale [B,M,Hq] (or None) and kv_scale
+    [B,N]."""
+    B, M, Hq, Dqk = _rank(q, "q", 4)
+    N = _rank(kv, "kv", 3)[1]
+    K = _rank(topk_idxs, "topk_idxs", 3)[2]
+    _tensor(q, "q", _FP8, (B, M, Hq, Dqk))
+    _tensor(q_scale, "q_scale", _F32, (B, M, Hq))
+    _tensor(kv, "kv", _FP8, (B, N, Dqk))
+    if kv_scale is None:
+        raise ValueError("kv_scale is required")
+    _tensor(kv_scale, "kv_scale", _F32, (B, N))
+    _tensor(attn_sink, "attn_sink", _F32, (Hq,))
+    _tensor(topk_idxs, "topk_idxs", _I32, (B, M, K))
+    _tensor(out, "out", _BF16, (B, M, Hq, dv))
+    _same_device(q, q_scale, kv, kv_scale, attn_sink, topk_idxs, out)
+    if out is None:
+        out = torch.empty((B, M, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    with torch.cuda.device(q.device):
+        need = (sparse_attn_fp8_workspace_size(B, M, Hq, Dqk, dv, K)
+                if isinstance(workspace, str) else 0)
+        wp, wn, _keep = _workspace(workspace, need, q.device)
+        _check("dsa_sparse_attn_fwd_fp8", lib().dsa_sparse_attn_fwd_fp8(
+            _ptr(q), _ptr(q_scale), _ptr(kv), _ptr(kv_scale), _ptr(attn_sink),
+            _ptr(topk_idxs), _ptr(out), B, M, N, Hq, Dqk, dv, K, float(sm_scale), wp, wn,
+            _stream(q)))
     return out
 
 

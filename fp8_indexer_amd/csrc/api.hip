@@ -187,6 +187,61 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv, dsa_kv_dtype kv_dt
 
 namespace {
 
+dsa_status check_attn_fp8(const void* q, const float* q_scale, const void* kv,
+                          const float* kv_scale, const float* sink, const int32_t* idx,
+                          const void* o, int64_t B, int64_t M, int64_t N, int32_t Hq,
+                          int32_t Dqk, int32_t Dv, int32_t K) {
+  if (!q || !kv || !kv_scale || !idx || !o) return DSA_ERR_INVALID_VALUE;
+  if (B <= 0 || M <= 0 || N <= 0 || Hq <= 0 || Dqk <= 0 || Dv <= 0 || K <= 0 || Dv > Dqk)
+    return DSA_ERR_INVALID_VALUE;
+  if (B * M > kMaxI32 || N > kMaxI32 || B > kMaxI32 / N) return DSA_ERR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(o, 16) || !aligned(idx, 4) ||
+      !aligned(kv_scale, 4) || (q_scale && !aligned(q_scale, 4)) || (sink && !aligned(sink, 4)))
+    return DSA_ERR_INVALID_VALUE;
+  if (K > 4096 || !dsa::attn_fp8_supported(Hq, Dqk, Dv)) return DSA_ERR_NOT_SUPPORTED;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_sparse_attn_fp8_workspace_size(int64_t B, int64_t M, int32_t Hq, int32_t Dqk,
+                                              int32_t Dv, int32_t K, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_VALUE;
+  alignas(16) static const int64_t dummy[2] = {0, 0};  // stand-in pointers: never dereferenced
+  const float* fdummy = reinterpret_cast<const float*>(dummy);
+  const dsa_status st = check_attn_fp8(dummy, nullptr, dummy, fdummy, nullptr,
+                                       reinterpret_cast<const int32_t*>(dummy), dummy, B, M, 1,
+                                       Hq, Dqk, Dv, K);
+  if (st != DSA_OK) return st;
+  const dsa::AttnFp8Args a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           B, M, 1, Hq, Dqk, Dv, K, 0.f};
+  *bytes = dsa::attn_fp8_workspace_bytes(a);
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_fwd_fp8(const void* q, const float* q_scale, const void* kv,
+                                   const float* kv_scale, const float* attn_sink,
+                                   const int32_t* topk_idxs, void* o, int64_t B, int64_t M,
+                                   int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K,
+                                   float sm_scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  dsa_status st = check_attn_fp8(q, q_scale, kv, kv_scale, attn_sink, topk_idxs, o, B, M, N, Hq,
+                                 Dqk, Dv, K);
+  if (st != DSA_OK) return st;
+  const dsa::AttnFp8Args a{q, q_scale, kv, kv_scale, attn_sink, topk_idxs, o,
+                           B, M, N, Hq, Dqk, Dv, K, sm_scale};
+  st = check_workspace(workspace, workspace_bytes, dsa::attn_fp8_workspace_bytes(a));
+  if (st != DSA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(dsa::launch_attn_fp8(a, dsa::Workspace{workspace, workspace_bytes}, s), s);
+}
+
+}  // extern "C"
+
+namespace {
+
 // ---- indexer + top-k in slabs of rows -------------------------------------
 // The [B, M, N] logits never exist: rows are scored and selected in slabs
 // whose logits live in the workspace.  A slab is a group of whole batch

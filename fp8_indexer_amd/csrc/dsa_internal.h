@@ -65,6 +65,20 @@ struct AttnBwdArgs {
   float sm_scale;
 };
 
+// Full-FP8 attention: q and kv hold e4m3fn codes.
+struct AttnFp8Args {
+  const void* q;
+  const float* q_scale;   // [B, M, Hq] or NULL (= 1)
+  const void* kv;
+  const float* kv_scale;  // [B, N]
+  const float* attn_sink;
+  const int32_t* topk_idxs;
+  void* o;
+  int64_t B, M, N;
+  int Hq, Dqk, Dv, K;
+  float sm_scale;
+};
+
 bool indexer_supported(int H, int D);
 bool attn_bwd_supported(int Hq, int Dqk, int Dv);
 
@@ -87,5 +101,15 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, Workspace ws, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
+bool attn_fp8_supported(int Hq, int Dqk, int Dv);
+size_t attn_fp8_workspace_bytes(const AttnFp8Args& a);
+hipError_t launch_attn_fp8(const AttnFp8Args& a, Workspace ws, hipStream_t stream);
+
+// Merge of split partial results (bf16 O_s / l_s [rows, S, Hq, Dv], then
+// fp32 (m_s, l_s) [rows, S, Hq], m in log2 units) into bf16 o.
+hipError_t launch_attn_merge(const uint16_t* wso, const float2* wsml, const float* sink,
+                             uint16_t* o, long long rows, int Hq, int Dv, int S,
+                             hipStream_t stream);
 
 }  // namespace dsa

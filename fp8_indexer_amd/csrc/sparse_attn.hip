@@ -834,10 +834,7 @@ hipError_t launch(const AttnArgs& a, Workspace ws, hipStream_t stream) {
                      wsml);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int HPB = 256 / (DV / 4);
-  hipLaunchKernelGGL((attn_merge_kernel<DV>), dim3((unsigned)(rows * (a.Hq / HPB))), dim3(256), 0,
-                     stream, wso, wsml, a.attn_sink, (uint16_t*)a.o, a.Hq, S);
-  return hipGetLastError();
+  return launch_attn_merge(wso, wsml, a.attn_sink, (uint16_t*)a.o, rows, a.Hq, DV, S, stream);
 }
 
 // Heads per wave at 128 heads (tuning knob: 32 -> 4 waves, 16 -> 8 waves).
@@ -857,6 +854,25 @@ hipError_t launch_heads(const AttnArgs& a, Workspace ws, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_attn_merge(const uint16_t* wso, const float2* wsml, const float* sink,
+                             uint16_t* o, long long rows, int Hq, int Dv, int S,
+                             hipStream_t stream) {
+  if (Dv == 512) {
+    constexpr int HPB = 256 / (512 / 4);
+    if (Hq % HPB != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_merge_kernel<512>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
+                       0, stream, wso, wsml, sink, o, Hq, S);
+  } else if (Dv == 64) {
+    constexpr int HPB = 256 / (64 / 4);
+    if (Hq % HPB != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_merge_kernel<64>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
+                       0, stream, wso, wsml, sink, o, Hq, S);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool attn_supported(int Hq, int Dqk, int Dv, bool fp8) {
   if (!(Hq == 16 || Hq == 32 || Hq == 64 || Hq == 128)) return false;

@@ -1,0 +1,556 @@
+// sparse_attn_fp8.hip -- full-FP8 gathered sparse attention forward with a
+// sink, gfx950.
+//
+// Semantics: the sparse attention of the DeepSeek V4.1 atlas page
+// (sparse_attn_kernel / sparse_attn: gather the top-k KV rows by index, online
+// softmax, attn_sink in the denominator only, -1 masked, zero output for a row
+// without a valid index) with an e4m3 query and KV cache and a bf16 output,
+// as in the TileLang "deepseek_v32" page, section "Sparse MLA Forward (FP8)".
+// Values: q = code * q_scale[b,t,h], kv = code * kv_scale[b,j].  Both
+// products run on fp8 MFMA; the probabilities enter PV as e4m3, scaled up
+// before the cast so that they use the format's range (the scaling by the
+// e4m3 maximum, 448, proposed in the FlashInfer MLA pull-request discussion,
+// with the output divided by the same factor).
+//
+// Design (MI355X-first):
+//  * v_mfma_f32_32x32x64_f8f6f4 for both products (measured on gfx950: 4.7
+//    of the 5.0 PFLOP/s fp8 peak; the older 16x16x32 fp8 MFMA runs at only
+//    the bf16 rate).  Lane l holds A row l%32 / B column l%32 and bytes
+//    [32*(l/32), +32) of the 64-deep k-step; C lane l holds column l%32, rows
+//    8i + 4*(l/32) + j in register 4i + j.
+//  * One workgroup of 4 waves per query token (per split of its indices).
+//    QK^T is formed transposed, S^T[j, h] = kv_j . q_h, with q as the B
+//    operand in registers (72 VGPRs for 32 heads and 576 dims).  With 128
+//    heads each wave owns a 32-head tile and both 32-row halves of a 64-row
+//    KV tile; with 64 heads two waves share a head tile and take one half
+//    each.
+//  * PV contracts over 64 gathered rows per MFMA: O^T[c, h] += V^T[c, k]
+//    P^T[k, h].  The P^T B-fragment is the QK^T C-fragment itself (lane (h,
+//    g) holds its 32 rows' probabilities as 32 e4m3 bytes) once the MFMA row
+//    of each gathered row is chosen so that the V^T A-fragment can be read
+//    with gfx950's 8-bit transposing LDS load (ds_read_b64_tr_b8: in each
+//    16-lane group, lanes 2r and 2r+1 give the address of row r's 16 bytes
+//    and lane i receives byte i of all 8 rows).  The row permutation pi
+//    below also keeps both LDS reads free of bank conflicts.  This replaces
+//    the K-major V copy that the TileLang page builds in shared memory.
+//  * All 4 waves share P through LDS and split the 512 output columns, so
+//    each V fragment feeds one MFMA per 32-head tile and O (128 heads x 128
+//    columns per wave) fills the AGPRs.
+//  * KV tiles of 64 rows (576 bytes each, row stride 608 bytes) are gathered
+//    into VGPRs while the current tile's QK^T runs and written to the other
+//    LDS buffer after the softmax (double buffering, two barriers per tile).
+//  * Softmax in base 2 with sm_scale*log2(e) and q_scale folded into one
+//    per-head factor.  The exponent reference of each head is the first
+//    tile's max and is never moved, so O is only ever touched by MFMA; P is
+//    2^(x - ref) * 16 * kv_scale_j / sigma (sigma = the largest kv_scale of
+//    the row's indices) before the e4m3 cast.  If some score exceeds its
+//    reference by more than log2(28) (P could pass the e4m3 maximum), the
+//    workgroup restarts the token with a max-only pre-pass and a final pass
+//    at the exact max with P = 2^(x - max) * 448 * kv_scale_j / sigma.  The
+//    denominator sums the unrounded 2^(x - ref).
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int kDqk = 576, kDv = 512;
+constexpr int kBI = 64;                  // gathered rows per tile
+constexpr int kRS = kDqk + 32;           // LDS row stride (bytes): 19 x 32
+constexpr int kTile = kBI * kRS;         // LDS tile (bytes)
+constexpr int kKS = kDqk / 64;           // 64-deep k-steps of QK^T
+constexpr int kCPR = kDqk / 16;          // 16-byte chunks per row
+constexpr int kThreads = 256;
+constexpr int kNC = kBI * kCPR / kThreads;  // staged chunks per thread and tile
+constexpr int kMaxK = 4096;
+constexpr int kMaxTiles = kMaxK / kBI;
+constexpr int kOTW = kDv / 32 / 4;       // 32-column O tiles per wave
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kP0 = 16.f;              // P factor of the first pass
+constexpr float kPMax = 448.f;           // P factor of the exact-max pass
+constexpr float kHeadroom = 4.8f;        // < log2(448 / kP0)
+static_assert(kBI * kCPR % kThreads == 0, "staging");
+static_assert(kRS % 64 == 32, "row stride: odd number of 32-byte units");
+
+__device__ __forceinline__ f32x16 mfma_f8_32x32x64(const i32x8& a, const i32x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// MFMA row r (0..31) of a 32-row half reads LDS row pi(r) of that half.  A
+// lane (h, g) of the C layout holds rows 8i + 4g + j; with pi its rows for
+// i in {2p, 2p+1} are 8 rows distinct mod 8 (one transposing read without
+// bank conflicts), and MFMA rows 8m..8m+7 stay 8 LDS rows distinct mod 8
+// (the QK^T operand read).
+__device__ __forceinline__ int pi_row(int r) { return r ^ ((r >> 1) & 4); }
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+}
+
+// Four fp32 -> four e4m3fn bytes (round to nearest even, a in byte 0; a
+// value above 464 gives the NaN code).
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+template <int HQ, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale,
+    const float* __restrict__ sink, const int* __restrict__ idx, uint16_t* __restrict__ o,
+    int M, int N, int K, float scale_log2, int S, int kspan, uint16_t* __restrict__ wso,
+    float2* __restrict__ wsml) {
+  static_assert(HQ == 64 || HQ == 128, "heads");
+  constexpr int TS = 128 / HQ;   // waves per head tile (each takes 2/TS row halves)
+  constexpr int NT = 2 / TS;     // 32-row halves per wave
+  constexpr int NHT = HQ / 32;   // 32-head tiles
+  __shared__ __align__(16) uint8_t sKV[2][kTile];
+  __shared__ int sIdx[kMaxK];
+  __shared__ int sList[kMaxTiles], sFirst[kMaxTiles], sFull[kMaxTiles];
+  __shared__ __align__(16) float sSc[2][kBI];     // kv_scale of each row (0: invalid slot)
+  __shared__ __align__(16) i32x8 sP[NHT][kWave];  // P^T fragments
+  __shared__ float sMx[TS][HQ], sLs[TS][HQ], sMf[HQ];
+  __shared__ float sRed[kThreads / kWave];
+  __shared__ int sNvt, sFlag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, hl = lane & 31;
+  const int qht = wave / TS;                 // head tile of this wave's QK^T
+  const int tau0 = TS == 2 ? wave % 2 : 0;   // first row half of this wave
+  const int hq = qht * 32 + hl;              // this lane's head in QK^T / softmax
+  const int c0 = wave * (kDv / 4);           // first output column of this wave's PV
+
+  const int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
+  const int split = (int)(blockIdx.x % S);
+  const int b = rtok / M;
+  const int kbeg = split * kspan;
+  const int klen = max(0, min(K - kbeg, kspan));
+  const int ntiles = (klen + kBI - 1) / kBI;
+  const int nidx = ntiles * kBI;
+
+  // ---- prologue -------------------------------------------------------------
+  // q fragments: lane (h, g) holds bytes [64s + 32g, +32) of its head's row
+  i32x8 qf[kKS];
+  {
+    const uint8_t* qrow = q + ((size_t)rtok * HQ + hq) * kDqk + 32 * g;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(qrow + 64 * s);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(qrow + 64 * s + 16);
+      qf[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  const float qsl = (q_scale ? q_scale[(size_t)rtok * HQ + hq] : 1.f) * scale_log2;
+  // indices (sanitised: -1 = invalid) and the largest kv_scale among them
+  const int* ridx = idx + (size_t)rtok * K + kbeg;
+  const float* ksb = kv_scale + (size_t)b * N;
+  float smax = 0.f;
+  for (int p = tid; p < nidx; p += kThreads) {
+    int v = p < klen ? ridx[p] : -1;
+    v = (v >= 0 && v < N) ? v : -1;
+    sIdx[p] = v;
+    if (v >= 0) smax = fmaxf(smax, ksb[v]);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) smax = fmaxf(smax, __shfl_xor(smax, sh, kWave));
+  if (lane == 0) sRed[wave] = smax;
+  __syncthreads();
+  float sigma = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) sigma = fmaxf(sigma, sRed[w]);
+  const float inv_sigma = sigma > 0.f ? 1.f / sigma : 1.f;
+  // per tile: first valid index (invalid slots gather that row) and fullness
+  for (int t = tid; t < ntiles; t += kThreads) {
+    int first = -1;
+    bool full = true;
+    for (int r = kBI - 1; r >= 0; --r) {
+      const int v = sIdx[t * kBI + r];
+      first = v >= 0 ? v : first;
+      full = full && v >= 0;
+    }
+    sFirst[t] = first;
+    sFull[t] = full;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+      const int t = t0 + lane;
+      const bool f = t < ntiles && sFirst[t] >= 0;
+      const uint64_t mk = __ballot(f);
+      if (f) sList[base + __popcll(mk & lt)] = t;
+      base += __popcll(mk);
+    }
+    if (lane == 0) sNvt = base;
+  }
+  __syncthreads();
+  const int nvt = sNvt;
+
+  // ---- staging: chunk k of this thread is chunk tid + 256k of the tile ------
+  i32x4 pre[kNC];
+  int grow[kNC];
+  float pscale = 0.f;
+  const uint8_t* kvb = kv + (size_t)b * N * kDqk;
+  auto gload = [&](int tile) {
+    const int* ti = sIdx + tile * kBI;
+    const int first = sFirst[tile];
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+      const int c = tid + kThreads * k;
+      const int row = ti[c / kCPR];
+      grow[k] = row >= 0 ? row : first;
+    }
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+      const int c = tid + kThreads * k;
+      pre[k] = *reinterpret_cast<const i32x4*>(kvb + (size_t)grow[k] * kDqk + (c % kCPR) * 16);
+    }
+    if (tid < kBI) {
+      const int row = ti[tid];
+      pscale = row >= 0 ? ksb[row] : 0.f;
+    }
+  };
+  auto lstore = [&](uint8_t* dst, float* dsc) {
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+      const int c = tid + kThreads * k;
+      *reinterpret_cast<i32x4*>(dst + (c / kCPR) * kRS + (c % kCPR) * 16) = pre[k];
+    }
+    if (tid < kBI) dsc[tid] = pscale;
+  };
+
+  // ---- per-tile pieces --------------------------------------------------------
+  f32x16 oacc[NHT][kOTW];
+#pragma unroll
+  for (int oh = 0; oh < NHT; ++oh)
+#pragma unroll
+    for (int t = 0; t < kOTW; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[oh][t][e] = 0.f;
+  float m = -1e30f;  // exponent reference of head hq (log2 units)
+  float lsum = 0.f;  // this lane's share of sum 2^(x - m)
+  float xmax = -INFINITY;  // largest x - m seen (first pass: overflow check)
+
+  // QK^T of row half tau: S^T rows r = MFMA rows, LDS rows 32 tau + pi(r)
+  auto qk = [&](const uint8_t* sK, int tau) {
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const uint8_t* arow = sK + (32 * tau + pi_row(hl)) * kRS + 32 * g;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + 64 * s);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + 64 * s + 16);
+      const i32x8 a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = mfma_f8_32x32x64(a, qf[s], acc);
+    }
+    return acc;
+  };
+  // LDS row of C register 4i + j of row half tau for this lane
+  auto crow = [&](int tau, int i, int j) { return 32 * tau + pi_row(8 * i + 4 * g + j); };
+
+  // V^T A-fragment of output column tile t: slot 8q + r of lane half g is LDS
+  // row 32(q>>1) + pi(8(2(q&1) + (r>>2)) + 4g + (r&3)), r = the row the
+  // lane pair (2r, 2r+1) of each 16-lane group addresses.
+  const int l16 = lane & 15, trr = l16 >> 1;
+  const int vcol = c0 + 16 * ((lane >> 4) & 1) + 8 * (l16 & 1);
+  int voff[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+    voff[qq] = (32 * (qq >> 1) + pi_row(8 * (2 * (qq & 1) + (trr >> 2)) + 4 * g + (trr & 3))) * kRS +
+               vcol;
+  auto vfrag = [&](const uint8_t* sK, int t) {
+    const i32x2 r0 = lds_read_tr8(sK + voff[0] + 32 * t);
+    const i32x2 r1 = lds_read_tr8(sK + voff[1] + 32 * t);
+    const i32x2 r2 = lds_read_tr8(sK + voff[2] + 32 * t);
+    const i32x2 r3 = lds_read_tr8(sK + voff[3] + 32 * t);
+    return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  };
+
+  // mode 0: reference = max of the first tile, P factor 16;
+  // mode 1: max-only pre-pass; mode 2: exact max, P factor 448.
+  int mode = 0;
+#pragma unroll 1
+  for (;;) {
+    if (tid == 0) sFlag = 0;
+    const float pf = (mode == 2 ? kPMax : kP0) * inv_sigma;
+    if (nvt > 0) {
+      gload(sList[0]);
+      lstore(sKV[0], sSc[0]);
+    }
+#pragma unroll 1
+    for (int it = 0; it < nvt; ++it) {
+      const uint8_t* cur = sKV[it & 1];
+      const float* curS = sSc[it & 1];
+      const int tile = sList[it];
+      __syncthreads();  // tile it complete; the other buffer and sP are free
+      const bool more = it + 1 < nvt;
+      if (more) gload(sList[it + 1]);
+      f32x16 sacc[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) sacc[u] = qk(cur, tau0 + u);
+      // x = score * sm_scale * log2(e) (q_scale folded in), -inf if masked
+      float xv[NT][16];
+      const bool full = sFull[tile] != 0;
+      const int* ti = sIdx + tile * kBI;
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = crow(tau0 + u, i, j);
+            const float x = sacc[u][4 * i + j] * (qsl * curS[r]);
+            xv[u][4 * i + j] = (full || ti[r] >= 0) ? x : -INFINITY;
+          }
+      if (mode == 1 || (mode == 0 && it == 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, xv[u][e]);
+        mx = fmaxf(mx, wave_xor(mx, 32));
+        if (mode == 1) {
+          m = fmaxf(m, mx);
+        } else {
+          if constexpr (TS == 2) {
+            if (g == 0) sMx[tau0][hq] = mx;
+            __syncthreads();
+            mx = fmaxf(sMx[0][hq], sMx[1][hq]);
+          }
+          m = mx;  // the first tile holds a valid index: finite
+        }
+      }
+      if (mode != 1) {
+        int pk[NT][4];
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float t = xv[u][4 * i + j] - m;
+              if (mode == 0) xmax = fmaxf(xmax, t);
+              const float e = fast_exp2(t);
+              lsum += e;
+              p[j] = e * (curS[crow(tau0 + u, i, j)] * pf);
+            }
+            pk[u][i] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+          }
+        // P^T bytes 16 tau + 4i + j of lane (h, g) <- C register 4i + j
+        int* dstp = reinterpret_cast<int*>(&sP[qht][lane]);
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+          *reinterpret_cast<i32x4*>(dstp + 4 * (tau0 + u)) =
+              i32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
+      }
+      if (more) lstore(sKV[(it + 1) & 1], sSc[(it + 1) & 1]);
+      __syncthreads();  // P visible
+      if (mode != 1) {
+        i32x8 pb[NHT];
+#pragma unroll
+        for (int oh = 0; oh < NHT; ++oh) pb[oh] = sP[oh][lane];
+#pragma unroll
+        for (int t = 0; t < kOTW; ++t) {
+          const i32x8 va = vfrag(cur, t);
+#pragma unroll
+          for (int oh = 0; oh < NHT; ++oh) oacc[oh][t] = mfma_f8_32x32x64(va, pb[oh], oacc[oh][t]);
+        }
+      }
+    }
+    if (mode == 0 && __ballot(xmax > kHeadroom) != 0ull && lane == 0) sFlag = 1;
+    if (mode == 1) {
+      // exact max of each head: both row halves
+      if constexpr (TS == 2) {
+        if (g == 0) sMx[tau0][hq] = m;
+      }
+    }
+    __syncthreads();
+    const bool restart = sFlag != 0;
+    if (mode == 1 || restart) {
+      if (mode == 1) {
+        if constexpr (TS == 2) m = fmaxf(sMx[0][hq], sMx[1][hq]);
+        mode = 2;
+      } else {
+        mode = 1;
+        m = -INFINITY;
+      }
+      lsum = 0.f;
+      xmax = -INFINITY;
+#pragma unroll
+      for (int oh = 0; oh < NHT; ++oh)
+#pragma unroll
+        for (int t = 0; t < kOTW; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[oh][t][e] = 0.f;
+      __syncthreads();  // the flag reset below is not seen early
+      continue;
+    }
+    break;
+  }
+
+  // ---- sink, normalise, store -------------------------------------------------
+  // l of each head: this lane's share, both lane halves, both row halves
+  {
+    const float l = lsum + wave_xor(lsum, 32);
+    if (g == 0) {
+      sLs[tau0][hq] = l;
+      if (tau0 == 0) sMf[hq] = m;
+    }
+  }
+  __syncthreads();
+  // O holds sum_j e4m3(2^(x_j - m) kv_scale_j pf) * code_j: o = O / (pf l)
+  const float pf_out = (mode == 2 ? kPMax : kP0) * inv_sigma;
+  float inv[NHT];
+#pragma unroll
+  for (int oh = 0; oh < NHT; ++oh) {
+    const int h = oh * 32 + hl;
+    float l = sLs[0][h];
+    if constexpr (TS == 2) l += sLs[1][h];
+    const float mh = sMf[h];
+    if constexpr (SPLIT) {
+      if (wave == 0 && g == 0) wsml[((size_t)rtok * S + split) * HQ + h] = float2{mh, l};
+    } else {
+      if (sink) l += fast_exp2(sink[h] * kLog2e - mh);
+    }
+    inv[oh] = l > 0.f ? __builtin_amdgcn_rcpf(l * pf_out) : 0.f;
+  }
+  if constexpr (SPLIT) {
+    // this split's O / l in bf16 (0 without a valid index), straight from
+    // the C layout: lane (h, g) holds columns c0 + 32t + 8i + 4g + j
+    const size_t part = (size_t)rtok * S + split;
+#pragma unroll
+    for (int oh = 0; oh < NHT; ++oh) {
+      uint16_t* orow = wso + (part * HQ + oh * 32 + hl) * kDv + c0 + 4 * g;
+#pragma unroll
+      for (int t = 0; t < kOTW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& v = oacc[oh][t];
+          uint2 pk2;
+          pk2.x = pack_bf16x2(v[4 * i] * inv[oh], v[4 * i + 1] * inv[oh]);
+          pk2.y = pack_bf16x2(v[4 * i + 2] * inv[oh], v[4 * i + 3] * inv[oh]);
+          *reinterpret_cast<uint2*>(orow + 32 * t + 8 * i) = pk2;
+        }
+    }
+  } else {
+    // bf16 O through LDS (the KV buffers, free now) in passes of 64 heads so
+    // that each head row of o is written whole with 16-byte lanes
+    constexpr int OS = kDv + 8;  // row stride (elements): 16-byte aligned rows
+    constexpr int ORP = 64;      // head rows per pass
+    static_assert(ORP * OS * 2 <= (int)sizeof(sKV), "O staging");
+    uint16_t* so = reinterpret_cast<uint16_t*>(&sKV[0][0]);
+#pragma unroll
+    for (int pass = 0; pass < HQ / ORP; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's rows are read
+#pragma unroll
+      for (int oh = 0; oh < NHT; ++oh) {
+        const int hr = oh * 32 - pass * ORP;
+        if (hr >= 0 && hr < ORP) {
+          uint16_t* srow = so + (hr + hl) * OS + c0 + 4 * g;
+#pragma unroll
+          for (int t = 0; t < kOTW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x16& v = oacc[oh][t];
+              uint2 pk2;
+              pk2.x = pack_bf16x2(v[4 * i] * inv[oh], v[4 * i + 1] * inv[oh]);
+              pk2.y = pack_bf16x2(v[4 * i + 2] * inv[oh], v[4 * i + 3] * inv[oh]);
+              *reinterpret_cast<uint2*>(srow + 32 * t + 8 * i) = pk2;
+            }
+        }
+      }
+      __syncthreads();
+      uint16_t* obase = o + ((size_t)rtok * HQ + pass * ORP) * kDv;
+      for (int u = tid; u < ORP * (kDv / 8); u += kThreads) {
+        const int r = u / (kDv / 8), c8 = u % (kDv / 8);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * kDv + c8 * 8) =
+            *reinterpret_cast<const i32x4*>(so + r * OS + c8 * 8);
+      }
+    }
+  }
+}
+
+// Splits of each row's K indices (decode: B*M at most half the compute
+// units): S workgroups per row, at least 4 tiles each.  Returns S (1:
+// unsplit) and the span of each split.
+int fp8_splits(const AttnFp8Args& a, int& kspan) {
+  const long long rows = a.B * a.M;
+  const int cus = device_cus();
+  int S = 1;
+  kspan = a.K;
+  if (rows * 2 <= cus) {
+    const int want = (int)((cus + rows - 1) / rows);
+    const int max_s = max(1, a.K / (4 * kBI));
+    S = min(want, max_s);
+    kspan = (a.K + S - 1) / S;
+    kspan = (kspan + kBI - 1) / kBI * kBI;
+    S = (a.K + kspan - 1) / kspan;
+  }
+  return S;
+}
+
+size_t fp8_split_bytes(const AttnFp8Args& a, int S) {
+  if (S <= 1) return 0;
+  return (size_t)(a.B * a.M) * S * a.Hq * (a.Dv * sizeof(uint16_t) + sizeof(float2));
+}
+
+template <int HQ>
+hipError_t launch_fp8(const AttnFp8Args& a, Workspace ws, hipStream_t stream) {
+  const long long rows = a.B * a.M;
+  if (rows > 0x7fffffffLL || a.K > kMaxK || a.Hq != HQ) return hipErrorInvalidValue;
+  const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)kDqk);
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  int kspan;
+  int S = fp8_splits(a, kspan);
+  if (S > 1 && (ws.ptr == nullptr || ws.bytes < fp8_split_bytes(a, S))) {
+    S = 1;
+    kspan = a.K;
+  }
+  const uint8_t* q = static_cast<const uint8_t*>(a.q);
+  const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
+  if (S == 1) {
+    hipLaunchKernelGGL((sparse_attn_fp8_kernel<HQ, false>), dim3((unsigned)rows), dim3(kThreads),
+                       0, stream, q, a.q_scale, kv, a.kv_scale, a.attn_sink, a.topk_idxs,
+                       (uint16_t*)a.o, (int)a.M, (int)a.N, a.K, scale_log2, 1, a.K, nullptr,
+                       nullptr);
+    return hipGetLastError();
+  }
+  uint16_t* wso = static_cast<uint16_t*>(ws.ptr);
+  float2* wsml = reinterpret_cast<float2*>(wso + (size_t)rows * S * HQ * kDv);
+  hipLaunchKernelGGL((sparse_attn_fp8_kernel<HQ, true>), dim3((unsigned)(rows * S)),
+                     dim3(kThreads), 0, stream, q, a.q_scale, kv, a.kv_scale, a.attn_sink,
+                     a.topk_idxs, (uint16_t*)a.o, (int)a.M, (int)a.N, a.K, scale_log2, S, kspan,
+                     wso, wsml);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_attn_merge(wso, wsml, a.attn_sink, (uint16_t*)a.o, rows, HQ, kDv, S, stream);
+}
+
+}  // namespace
+
+bool attn_fp8_supported(int Hq, int Dqk, int Dv) {
+  return (Hq == 64 || Hq == 128) && Dqk == kDqk && Dv == kDv;
+}
+
+size_t attn_fp8_workspace_bytes(const AttnFp8Args& a) {
+  int kspan;
+  return fp8_split_bytes(a, fp8_splits(a, kspan));
+}
+
+hipError_t launch_attn_fp8(const AttnFp8Args& a, Workspace ws, hipStream_t stream) {
+  if (a.Dqk != kDqk || a.Dv != kDv) return hipErrorInvalidValue;
+  if (a.Hq == 128) return launch_fp8<128>(a, ws, stream);
+  if (a.Hq == 64) return launch_fp8<64>(a, ws, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

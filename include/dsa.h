@@ -6,8 +6,9 @@
  *   2. dsa_topk            -- exact per-row top-k over those scores
  *   3. dsa_sparse_attn_fwd -- gathered sparse attention forward with a sink
  *   4. dsa_prefill         -- 1 -> 2 -> 3 on one stream
- * and dsa_indexer_topk (1 + 2 without the logits buffer) and
- * dsa_sparse_attn_bwd (the gradients of 3).
+ * and dsa_indexer_topk (1 + 2 without the logits buffer),
+ * dsa_sparse_attn_fwd_fp8 (3 with an fp8 query and KV cache: full-FP8
+ * attention) and dsa_sparse_attn_bwd (the gradients of 3).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -23,7 +24,7 @@
  *    library allocates no device memory, keeps no pointer after a call
  *    returns and holds no mutable global state other than a mutex-guarded
  *    cache of each device's compute-unit count; calls are thread-safe.
- *    Calls that can use scratch (dsa_topk, dsa_sparse_attn_fwd, dsa_prefill)
+ *    Calls that can use scratch (dsa_topk, dsa_sparse_attn_fwd[_fp8], dsa_prefill)
  *    take a `workspace` pointer and its size in bytes; the matching
  *    *_workspace_size call gives the bytes the fastest path needs for a
  *    shape on the current device.  A NULL workspace (or a size of 0 bytes
@@ -212,6 +213,47 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* kv,
                                int32_t Dv, int32_t K, float sm_scale,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * dsa_sparse_attn_fwd_fp8 -- full-FP8 sparse attention forward: the
+ * attention of dsa_sparse_attn_fwd with an e4m3 query and KV cache and a
+ * bf16 output (TileLang "deepseek_v32" examples page, section "Sparse MLA
+ * Forward (FP8)"), both products on fp8 MFMA.  The values are
+ *   q[b,t,h,d] = e4m3(q codes) * q_scale[b,t,h]   (q_scale NULL: 1)
+ *   kv[b,j,d]  = e4m3(kv codes) * kv_scale[b,j]
+ * and o is defined by the formula of dsa_sparse_attn_fwd on those values
+ * (sink, -1 / out-of-range indices and rows without a valid index alike).
+ * Rounding: QK^T is exact products with fp32 accumulation; the softmax runs
+ * in base 2 in fp32; each probability enters PV as an e4m3 number after
+ * scaling by 2^c * kv_scale[b,j] / sigma (sigma = the largest kv_scale of
+ * the row's indices, 2^c between 16 and 448 relative to the head's running
+ * reference, following the FlashInfer MLA pull-request discussion's
+ * scaling by the e4m3 maximum), so each term of o carries up to 2^-4
+ * relative error (plus e4m3 underflow below 2^-9 of the scaled maximum); the
+ * denominator sums unrounded fp32 probabilities; o is rounded to bf16.
+ *
+ *   q          [B, M, Hq, Dqk] e4m3fn codes
+ *   q_scale    [B, M, Hq] fp32 or NULL
+ *   kv         [B, N, Dqk]     e4m3fn codes
+ *   kv_scale   [B, N] fp32 (required)
+ *   attn_sink  [Hq] fp32 or NULL; topk_idxs [B, M, K] int32
+ *   o          [B, M, Hq, Dv] bf16 output
+ *   sm_scale   softmax scale; <= 0 selects 1/sqrt(Dqk)
+ * Supported: Hq in {64, 128}; (Dqk, Dv) = (576, 512); 1 <= K <= 4096.
+ * Workspace (dsa_sparse_attn_fp8_workspace_size): as dsa_sparse_attn_fwd,
+ * splits of each row's indices over S workgroups when B*M is at most half
+ * the device's compute units (S <= K/256); without a workspace the rows run
+ * unsplit, with the same result up to rounding.
+ */
+dsa_status dsa_sparse_attn_fp8_workspace_size(int64_t B, int64_t M, int32_t Hq, int32_t Dqk,
+                                              int32_t Dv, int32_t K, size_t* bytes);
+
+dsa_status dsa_sparse_attn_fwd_fp8(const void* q, const float* q_scale, const void* kv,
+                                   const float* kv_scale, const float* attn_sink,
+                                   const int32_t* topk_idxs, void* o, int64_t B, int64_t M,
+                                   int64_t N, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t K,
+                                   float sm_scale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * dsa_sparse_attn_bwd -- gradients of dsa_sparse_attn_fwd (bf16 kv).

@@ -23,7 +23,7 @@ def _lib():
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_four_stages():
@@ -139,6 +139,34 @@ def test_attention_rejects_bad_arguments():
     need = dsa.sparse_attn_workspace_size(1, 4, 128, 576, 512, 2048)
     if need > 0:
         assert call(ws=A16, wsb=need - 1) == WORKSPACE
+
+
+def test_fp8_attention_rejects_bad_arguments():
+    L = _lib()
+    f = L.dsa_sparse_attn_fwd_fp8
+
+    def call(q=A16, qs=None, kvs=A16, Hq=128, Dqk=576, Dv=512, K=2048, o=A16, ws=None, wsb=0,
+             M=4):
+        return f(q, qs, A16, kvs, None, A16, o, 1, M, 8, Hq, Dqk, Dv, K, 0.0, ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(kvs=None) == INVALID                  # the KV scales are required
+    assert call(qs=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(K=0) == INVALID
+    assert call(Dv=600) == INVALID
+    assert call(o=ctypes.c_void_p(0x10004)) == INVALID
+    assert call(Hq=32) == UNSUPPORTED
+    assert call(Hq=16) == UNSUPPORTED
+    assert call(Dqk=64, Dv=64) == UNSUPPORTED
+    assert call(K=5000) == UNSUPPORTED
+    need = dsa.sparse_attn_fp8_workspace_size(64, 1, 128, 576, 512, 2048)
+    assert need > 0
+    assert f(A16, None, A16, A16, None, A16, A16, 64, 1, 8, 128, 576, 512, 2048, 0.0, A16,
+             need - 1, None) == WORKSPACE
+    # 64-row tiles: at least 4 per split
+    S = need // (64 * 128 * (2 * 512 + 8))
+    assert need % (64 * 128 * (2 * 512 + 8)) == 0 and 2 <= S <= 2048 // 256
+    assert dsa.sparse_attn_fp8_workspace_size(1, 4096, 128, 576, 512, 2048) == 0
 
 
 def test_workspace_size_queries():

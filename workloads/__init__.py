@@ -15,6 +15,8 @@ depend on how many threads fill them):
   * indexer weights w: N(0, w_std) fp32 with w_std = H^-1/2;
   * attention q and kv: N(0,1) rounded to bf16 (RNE); for the fp8-KV workload
     kv is quantised per row like the indexer k and a per-row fp32 scale kept;
+    for the full-FP8 attention workloads q is also quantised, per (token,
+    head) row, with its fp32 scale kept;
   * attn_sink: N(0,1) fp32, one per attention head;
   * key windows: causal prefill ks = 0, ke = t+1; packed varlen ks = sequence
     start, ke = t+1; decode ks = 0, ke = L_b with L_b uniform in
@@ -46,6 +48,7 @@ class Workload:
     Dqk: int        # attention q/kv dim
     Dv: int         # attention output dim (first Dv dims of kv)
     kv_fp8: bool = False
+    q_fp8: bool = False       # attention q in e4m3 (full-FP8 attention)
     windows: str = "causal"   # causal | packed | decode
     seg: int = 0              # packed: sequence length
     decode_min: int = 4096
@@ -79,6 +82,16 @@ WORKLOADS = {
     "prefill_8192_fp8kv": Workload("prefill_8192_fp8kv", B=1, M=8192, N=8192,
                                    H=32, D=128, K=2048, Hq=64, Dqk=576, Dv=512,
                                    kv_fp8=True, seed=5),
+}
+
+
+# Full-FP8 attention (e4m3 q and kv): the shapes of the 4096-token prefill
+# (128 heads) and of the 8192-token fp8-KV prefill (64 heads).
+FP8_ATTN_WORKLOADS = {
+    "prefill_4096_fp8attn": WORKLOADS["prefill_4096"].with_(
+        name="prefill_4096_fp8attn", kv_fp8=True, q_fp8=True),
+    "prefill_8192_fp8attn": WORKLOADS["prefill_8192_fp8kv"].with_(
+        name="prefill_8192_fp8attn", q_fp8=True),
 }
 
 
@@ -148,8 +161,8 @@ def make_inputs(wl, parts=("indexer", "attn"), seed=None):
     numpy arrays:
       indexer: q8 [B,M,H,D] fp8, q_scale [B,M,H], k8 [B,N,D] fp8, k_scale [B,N],
                w [B,M,H]
-      attn:    q [B,M,Hq,Dqk] bf16, kv [B,N,Dqk] bf16 or fp8 (+ kv_scale [B,N]),
-               sink [Hq] fp32
+      attn:    q [B,M,Hq,Dqk] bf16, or fp8 with qa_scale [B,M,Hq] (q_fp8);
+               kv [B,N,Dqk] bf16 or fp8 (+ kv_scale [B,N]), sink [Hq] fp32
       always:  ks, ke [B,M] int32 (numpy), lengths (decode) or None"""
     import torch
     seed = wl.seed if seed is None else seed
@@ -177,7 +190,11 @@ def make_inputs(wl, parts=("indexer", "attn"), seed=None):
         out["w"] = torch.from_numpy(_normal(seed, 3, (B, M, wl.H), wl.w_std))
     if "attn" in parts:
         qa = _normal(seed, 4, (B, M, wl.Hq, wl.Dqk))
-        out["q"] = to_bf16(qa)
+        if wl.q_fp8:
+            out["q"], out["qa_scale"] = quantize_e4m3fn_rows(qa)
+        else:
+            out["q"] = to_bf16(qa)
+            out["qa_scale"] = None
         del qa
         kv = key_mask(_normal(seed, 5, (B, N, wl.Dqk)))
         if wl.kv_fp8:
