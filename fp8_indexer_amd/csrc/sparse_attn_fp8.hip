@@ -48,6 +48,8 @@
 //    workgroup restarts the token with a max-only pre-pass and a final pass
 //    at the exact max with P = 2^(x - max) * 448 * kv_scale_j / sigma.  The
 //    denominator sums the unrounded 2^(x - ref).
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -80,6 +82,22 @@ __device__ __forceinline__ f32x16 mfma_f8_32x32x64(const i32x8& a, const i32x8& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// QK^T MFMAs with the accumulator pinned to VGPRs, so that the O
+// accumulators of PV (compiler-scheduled MFMAs) have the AGPRs to
+// themselves: with both in AGPRs, 128 heads need more than a wave's 256.
+// Hazards the compiler cannot see through the asm: the accumulator is tied
+// (vdst = srcC), each MFMA is preceded by 2 wait states (VALU write -> MFMA
+// read), and qk_drain() gives the results 24 wait states before any VALU
+// reads them.
+__device__ __forceinline__ void qk_mfma(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+               : "+v"(acc)
+               : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_drain(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+}
+
 // MFMA row r (0..31) of a 32-row half reads LDS row pi(r) of that half.  A
 // lane (h, g) of the C layout holds rows 8i + 4g + j; with pi its rows for
 // i in {2p, 2p+1} are 8 rows distinct mod 8 (one transposing read without
@@ -109,11 +127,12 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   constexpr int TS = 128 / HQ;   // waves per head tile (each takes 2/TS row halves)
   constexpr int NT = 2 / TS;     // 32-row halves per wave
   constexpr int NHT = HQ / 32;   // 32-head tiles
-  __shared__ __align__(16) uint8_t sKV[2][kTile];
+  __shared__ __align__(16) uint8_t sKV[3][kTile];
   __shared__ int sIdx[kMaxK];
-  __shared__ int sList[kMaxTiles], sFirst[kMaxTiles], sFull[kMaxTiles];
-  __shared__ __align__(16) float sSc[2][kBI];     // kv_scale of each row (0: invalid slot)
-  __shared__ __align__(16) i32x8 sP[NHT][kWave];  // P^T fragments
+  __shared__ int sList[kMaxTiles], sFirst[kMaxTiles];
+  // per tile row: (kv_scale, score bias): (scale, 0) or (0, -inf) for an invalid slot
+  __shared__ __align__(16) float2 sSB[3][kBI];
+  __shared__ __align__(16) i32x8 sP[2][NHT][kWave];  // P^T fragments, double-buffered
   __shared__ float sMx[TS][HQ], sLs[TS][HQ], sMf[HQ];
   __shared__ float sRed[kThreads / kWave];
   __shared__ int sNvt, sFlag;
@@ -160,22 +179,20 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) smax = fmaxf(smax, __shfl_xor(smax, sh, kWave));
   if (lane == 0) sRed[wave] = smax;
+  if (tid == 0) sFlag = 0;
   __syncthreads();
   float sigma = 0.f;
 #pragma unroll
   for (int w = 0; w < kThreads / kWave; ++w) sigma = fmaxf(sigma, sRed[w]);
   const float inv_sigma = sigma > 0.f ? 1.f / sigma : 1.f;
-  // per tile: first valid index (invalid slots gather that row) and fullness
+  // per tile: the first valid index (invalid slots gather that row)
   for (int t = tid; t < ntiles; t += kThreads) {
     int first = -1;
-    bool full = true;
     for (int r = kBI - 1; r >= 0; --r) {
       const int v = sIdx[t * kBI + r];
       first = v >= 0 ? v : first;
-      full = full && v >= 0;
     }
     sFirst[t] = first;
-    sFull[t] = full;
   }
   __syncthreads();
   if (wave == 0) {
@@ -193,68 +210,146 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   __syncthreads();
   const int nvt = sNvt;
 
-  // ---- staging: chunk k of this thread is chunk tid + 256k of the tile ------
-  i32x4 pre[kNC];
-  int grow[kNC];
-  float pscale = 0.f;
+  // ---- staging: direct global -> LDS loads ---------------------------------
+  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS address M0 +
+  // 16 l (the instruction offset, 0 here, would be added to both
+  // addresses).  A tile buffer (64 rows x 608 bytes) is 38 blocks of 1 KiB;
+  // wave w fills blocks w, w+4, ...  A lane whose 16 bytes fall in a row's
+  // padding loads that row's first chunk (unused).  No VGPRs hold the tile
+  // on its way, and the loads complete while the other phase runs; the
+  // wait for them comes before the barrier that publishes the tile.
+  float2 psb = float2{0.f, -INFINITY};
   const uint8_t* kvb = kv + (size_t)b * N * kDqk;
-  auto gload = [&](int tile) {
+  constexpr int kBlocks = kTile / 1024;
+  static_assert(kTile % 1024 == 0, "tile blocks");
+  auto issue = [&](int tile, int buf) {
     const int* ti = sIdx + tile * kBI;
     const int first = sFirst[tile];
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-      const int c = tid + kThreads * k;
-      const int row = ti[c / kCPR];
-      grow[k] = row >= 0 ? row : first;
-    }
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-      const int c = tid + kThreads * k;
-      pre[k] = *reinterpret_cast<const i32x4*>(kvb + (size_t)grow[k] * kDqk + (c % kCPR) * 16);
-    }
     if (tid < kBI) {
       const int row = ti[tid];
-      pscale = row >= 0 ? ksb[row] : 0.f;
+      psb = row >= 0 ? float2{ksb[row], 0.f} : float2{0.f, -INFINITY};
     }
-  };
-  auto lstore = [&](uint8_t* dst, float* dsc) {
+    uint8_t* dst = &sKV[buf][0];
 #pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-      const int c = tid + kThreads * k;
-      *reinterpret_cast<i32x4*>(dst + (c / kCPR) * kRS + (c % kCPR) * 16) = pre[k];
+    for (int k = 0; k < (kBlocks + 3) / 4; ++k) {
+      const int bi = wave + 4 * k;
+      if (bi < kBlocks) {  // uniform over the wave
+        const int p16 = bi * 64 + lane;  // 16-byte unit of the tile buffer
+        const int r = p16 / (kRS / 16), u = p16 % (kRS / 16);
+        int row = ti[r];
+        row = row >= 0 ? row : first;
+        const uint8_t* src = kvb + (size_t)row * kDqk + (u < kCPR ? u * 16 : 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + bi * 1024),
+                                         16, 0, 0);
+      }
     }
-    if (tid < kBI) dsc[tid] = pscale;
   };
+  auto commit = [&](int buf) {
+    if (tid < kBI) sSB[buf][tid] = psb;
+  };
+  // vmcnt(0): every global load of this wave, the direct-to-LDS ones
+  // included, has landed
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0f70); };
 
   // ---- per-tile pieces --------------------------------------------------------
   f32x16 oacc[NHT][kOTW];
+  auto zero_o = [&]() {
 #pragma unroll
-  for (int oh = 0; oh < NHT; ++oh)
+    for (int oh = 0; oh < NHT; ++oh)
 #pragma unroll
-    for (int t = 0; t < kOTW; ++t)
+      for (int t = 0; t < kOTW; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[oh][t][e] = 0.f;
-  float m = -1e30f;  // exponent reference of head hq (log2 units)
-  float lsum = 0.f;  // this lane's share of sum 2^(x - m)
+        for (int e = 0; e < 16; ++e) oacc[oh][t][e] = 0.f;
+  };
+  zero_o();
+  float m = -1e30f;        // exponent reference of head hq (log2 units)
+  float lsum = 0.f;        // this lane's share of sum 2^(x - m)
   float xmax = -INFINITY;  // largest x - m seen (first pass: overflow check)
+  f32x16 sacc[NT];         // S^T of the tile in flight
 
-  // QK^T of row half tau: S^T rows r = MFMA rows, LDS rows 32 tau + pi(r)
-  auto qk = [&](const uint8_t* sK, int tau) {
-    f32x16 acc;
+  // QK^T of a tile: row half tau's MFMA row r reads LDS row 32 tau + pi(r).
+  // The A fragments of k-step s+1 are read before the MFMAs of step s, and
+  // a scheduling barrier keeps the compiler from hoisting every read (which
+  // would cost registers).
+  auto qk = [&](const uint8_t* sK) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    const uint8_t* arow = sK + (32 * tau + pi_row(hl)) * kRS + 32 * g;
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[u][e] = 0.f;
+    const uint8_t* abase = sK + (32 * tau0 + pi_row(hl)) * kRS + 32 * g;
+    i32x8 a[2][NT];
+    auto ld = [&](int s) {
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const uint8_t* arow = abase + 32 * u * kRS + 64 * s;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(arow);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + 16);
+        a[s & 1][u] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+    ld(0);
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + 64 * s);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + 64 * s + 16);
-      const i32x8 a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc = mfma_f8_32x32x64(a, qf[s], acc);
+      if (s + 1 < kKS) ld(s + 1);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) qk_mfma(sacc[u], a[s & 1][u], qf[s]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    return acc;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) qk_drain(sacc[u]);
   };
-  // LDS row of C register 4i + j of row half tau for this lane
-  auto crow = [&](int tau, int i, int j) { return 32 * tau + pi_row(8 * i + 4 * g + j); };
+  // C registers 4i..4i+3 of row half tau hold LDS rows 32 tau + pi(8i + 4g)
+  // + 0..3, which are consecutive: their (scale, bias) pairs are two
+  // 16-byte reads.
+  auto rowsb = [&](const float2* sb, int tau, int i, float2 (&v)[4]) {
+    const float4* p4 = reinterpret_cast<const float4*>(sb + 32 * tau + pi_row(8 * i + 4 * g));
+    const float4 a = p4[0], c = p4[1];
+    v[0] = float2{a.x, a.y};
+    v[1] = float2{a.z, a.w};
+    v[2] = float2{c.x, c.y};
+    v[3] = float2{c.z, c.w};
+  };
+  // largest x of the tile in flight for this lane's head (masked: -inf)
+  auto tile_max = [&](const float2* sb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float2 v[4];
+        rowsb(sb, tau0 + u, i, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(sacc[u][4 * i + j], qsl * v[j].x, v[j].y));
+      }
+    return fmaxf(mx, wave_xor(mx, 32));
+  };
+  // softmax of the tile in flight: P = 2^(x - m) * kv_scale * pf as e4m3,
+  // to this wave's bytes of the P^T fragments in dst
+  auto softmax = [&](const float2* sb, i32x8* dst, float pf) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      int pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float2 v[4];
+        rowsb(sb, tau0 + u, i, v);
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float t = fmaf(sacc[u][4 * i + j], qsl * v[j].x, v[j].y) - m;
+          xmax = fmaxf(xmax, t);
+          const float e = fast_exp2(t);
+          lsum += e;
+          p[j] = e * (v[j].x * pf);
+        }
+        pk[i] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+      }
+      // P^T bytes 16 tau + 4i + j of lane (h, g) <- C register 4i + j
+      *reinterpret_cast<i32x4*>(reinterpret_cast<int*>(&dst[qht * kWave + lane]) +
+                                4 * (tau0 + u)) = i32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
+  };
 
   // V^T A-fragment of output column tile t: slot 8q + r of lane half g is LDS
   // row 32(q>>1) + pi(8(2(q&1) + (r>>2)) + 4g + (r&3)), r = the row the
@@ -273,128 +368,106 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     const i32x2 r3 = lds_read_tr8(sK + voff[3] + 32 * t);
     return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   };
-
-  // mode 0: reference = max of the first tile, P factor 16;
-  // mode 1: max-only pre-pass; mode 2: exact max, P factor 448.
-  int mode = 0;
-#pragma unroll 1
-  for (;;) {
-    if (tid == 0) sFlag = 0;
-    const float pf = (mode == 2 ? kPMax : kP0) * inv_sigma;
-    if (nvt > 0) {
-      gload(sList[0]);
-      lstore(sKV[0], sSc[0]);
-    }
-#pragma unroll 1
-    for (int it = 0; it < nvt; ++it) {
-      const uint8_t* cur = sKV[it & 1];
-      const float* curS = sSc[it & 1];
-      const int tile = sList[it];
-      __syncthreads();  // tile it complete; the other buffer and sP are free
-      const bool more = it + 1 < nvt;
-      if (more) gload(sList[it + 1]);
-      f32x16 sacc[NT];
+  auto pv = [&](const uint8_t* sK, const i32x8* sPb) {
+    i32x8 pb[NHT];
 #pragma unroll
-      for (int u = 0; u < NT; ++u) sacc[u] = qk(cur, tau0 + u);
-      // x = score * sm_scale * log2(e) (q_scale folded in), -inf if masked
-      float xv[NT][16];
-      const bool full = sFull[tile] != 0;
-      const int* ti = sIdx + tile * kBI;
+    for (int oh = 0; oh < NHT; ++oh) pb[oh] = sPb[oh * kWave + lane];
+    i32x8 va[2];
+    va[0] = vfrag(sK, 0);
 #pragma unroll
-      for (int u = 0; u < NT; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = crow(tau0 + u, i, j);
-            const float x = sacc[u][4 * i + j] * (qsl * curS[r]);
-            xv[u][4 * i + j] = (full || ti[r] >= 0) ? x : -INFINITY;
-          }
-      if (mode == 1 || (mode == 0 && it == 0)) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, xv[u][e]);
-        mx = fmaxf(mx, wave_xor(mx, 32));
-        if (mode == 1) {
-          m = fmaxf(m, mx);
-        } else {
-          if constexpr (TS == 2) {
-            if (g == 0) sMx[tau0][hq] = mx;
-            __syncthreads();
-            mx = fmaxf(sMx[0][hq], sMx[1][hq]);
-          }
-          m = mx;  // the first tile holds a valid index: finite
-        }
-      }
-      if (mode != 1) {
-        int pk[NT][4];
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float t = xv[u][4 * i + j] - m;
-              if (mode == 0) xmax = fmaxf(xmax, t);
-              const float e = fast_exp2(t);
-              lsum += e;
-              p[j] = e * (curS[crow(tau0 + u, i, j)] * pf);
-            }
-            pk[u][i] = pack_fp8x4(p[0], p[1], p[2], p[3]);
-          }
-        // P^T bytes 16 tau + 4i + j of lane (h, g) <- C register 4i + j
-        int* dstp = reinterpret_cast<int*>(&sP[qht][lane]);
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-          *reinterpret_cast<i32x4*>(dstp + 4 * (tau0 + u)) =
-              i32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
-      }
-      if (more) lstore(sKV[(it + 1) & 1], sSc[(it + 1) & 1]);
-      __syncthreads();  // P visible
-      if (mode != 1) {
-        i32x8 pb[NHT];
-#pragma unroll
-        for (int oh = 0; oh < NHT; ++oh) pb[oh] = sP[oh][lane];
-#pragma unroll
-        for (int t = 0; t < kOTW; ++t) {
-          const i32x8 va = vfrag(cur, t);
-#pragma unroll
-          for (int oh = 0; oh < NHT; ++oh) oacc[oh][t] = mfma_f8_32x32x64(va, pb[oh], oacc[oh][t]);
-        }
-      }
-    }
-    if (mode == 0 && __ballot(xmax > kHeadroom) != 0ull && lane == 0) sFlag = 1;
-    if (mode == 1) {
-      // exact max of each head: both row halves
-      if constexpr (TS == 2) {
-        if (g == 0) sMx[tau0][hq] = m;
-      }
-    }
-    __syncthreads();
-    const bool restart = sFlag != 0;
-    if (mode == 1 || restart) {
-      if (mode == 1) {
-        if constexpr (TS == 2) m = fmaxf(sMx[0][hq], sMx[1][hq]);
-        mode = 2;
-      } else {
-        mode = 1;
-        m = -INFINITY;
-      }
-      lsum = 0.f;
-      xmax = -INFINITY;
+    for (int t = 0; t < kOTW; ++t) {
+      if (t + 1 < kOTW) va[(t + 1) & 1] = vfrag(sK, t + 1);
 #pragma unroll
       for (int oh = 0; oh < NHT; ++oh)
-#pragma unroll
-        for (int t = 0; t < kOTW; ++t)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[oh][t][e] = 0.f;
-      __syncthreads();  // the flag reset below is not seen early
-      continue;
+        oacc[oh][t] = mfma_f8_32x32x64(va[t & 1], pb[oh], oacc[oh][t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    break;
+  };
+
+  // Pipelined pass (mode 0: reference = the first tile's max, P factor 16;
+  // mode 2: the exact max, P factor 448).  Iteration it: | PV of tile it-1
+  // beside the softmax of tile it | QK^T of tile it+1 beside the LDS store
+  // of tile it+2 (gathered into VGPRs one iteration earlier) and the gather
+  // of tile it+3 |.  Three LDS tile buffers: tile i lives in buffer i % 3
+  // from its store (iteration i-2) to its PV (iteration i+1); the buffer
+  // tile it+2 is stored into held tile it-1, whose PV ends before the
+  // barrier that opens the second half.
+  auto pipelined = [&](int mode) {
+    const float pf = (mode == 2 ? kPMax : kP0) * inv_sigma;
+    if (nvt == 0) return;
+    __syncthreads();  // every wave is past its previous use of the buffers
+    issue(sList[0], 0);
+    wait_loads();
+    commit(0);
+    if (nvt > 1) {
+      issue(sList[1], 1);
+      wait_loads();
+      commit(1);
+    }
+    __syncthreads();
+    qk(sKV[0]);
+    if (mode == 0) {
+      float mx = tile_max(sSB[0]);
+      if constexpr (TS == 2) {
+        if (g == 0) sMx[tau0][hq] = mx;
+        __syncthreads();
+        mx = fmaxf(sMx[0][hq], sMx[1][hq]);
+      }
+      m = mx;  // the first tile holds a valid index: finite
+    }
+    int bc = 0;  // buffer of tile it: it % 3
+    auto step = [&](int it, auto later) {
+      const int bp = bc == 0 ? 2 : bc - 1, bn = bc == 2 ? 0 : bc + 1;
+      __syncthreads();  // P of tile it-1 visible
+      if constexpr (decltype(later)::value) pv(sKV[bp], &sP[(it - 1) & 1][0][0]);
+      softmax(sSB[bc], &sP[it & 1][0][0], pf);
+      if constexpr (decltype(later)::value) {
+        if (it + 1 < nvt) commit(bn);  // row scales of tile it+1, loaded in the last iteration
+      }
+      wait_loads();     // tile it+1 has landed in LDS
+      __syncthreads();  // P of tile it and tile it+1 visible; tile it-1's buffer free
+      qk(sKV[bn]);      // tile it+1 (past the last tile: unused)
+      if (it + 2 < nvt) issue(sList[it + 2], bp);
+      bc = bn;
+    };
+    step(0, std::false_type{});
+#pragma unroll 1
+    for (int it = 1; it < nvt; ++it) step(it, std::true_type{});
+    __syncthreads();  // P of the last tile visible
+    pv(sKV[bc == 0 ? 2 : bc - 1], &sP[(nvt - 1) & 1][0][0]);
+  };
+  // Max-only pass: the exact max of each head (one tile at a time).
+  auto prepass = [&]() {
+    m = -INFINITY;
+#pragma unroll 1
+    for (int it = 0; it < nvt; ++it) {
+      __syncthreads();  // the previous tile's QK^T is done
+      issue(sList[it], 0);
+      wait_loads();
+      commit(0);
+      __syncthreads();
+      qk(sKV[0]);
+      m = fmaxf(m, tile_max(sSB[0]));
+    }
+    if constexpr (TS == 2) {
+      if (g == 0) sMx[tau0][hq] = m;
+      __syncthreads();
+      m = fmaxf(sMx[0][hq], sMx[1][hq]);
+    }
+  };
+
+  int mode = 0;
+  pipelined(0);
+  if (__ballot(xmax > kHeadroom) != 0ull && lane == 0) sFlag = 1;
+  __syncthreads();
+  if (sFlag != 0) {
+    // some P could have passed the e4m3 range: exact max, then again
+    zero_o();
+    lsum = 0.f;
+    __syncthreads();  // every wave is past its last tile
+    prepass();
+    mode = 2;
+    pipelined(2);
   }
 
   // ---- sink, normalise, store -------------------------------------------------
