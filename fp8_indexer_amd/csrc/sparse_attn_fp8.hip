@@ -49,6 +49,7 @@
 //    at the exact max with P = 2^(x - max) * 448 * kv_scale_j / sigma.  The
 //    denominator sums the unrounded 2^(x - ref).
 #include <type_traits>
+#include <utility>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -62,12 +63,11 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kBI = 64;                  // gathered rows per tile
-constexpr int kRS = kDqk + 32;           // LDS row stride (bytes): 19 x 32
-constexpr int kTile = kBI * kRS;         // LDS tile (bytes)
+constexpr int kUnits = kDqk / 16;        // 16-byte units per row
+constexpr int kUS = kBI * 16 + 64;       // LDS stride of a unit (bytes): 64 rows + 64 pad
+constexpr int kTile = kUnits * kUS;      // LDS tile (bytes)
 constexpr int kKS = kDqk / 64;           // 64-deep k-steps of QK^T
-constexpr int kCPR = kDqk / 16;          // 16-byte chunks per row
 constexpr int kThreads = 256;
-constexpr int kNC = kBI * kCPR / kThreads;  // staged chunks per thread and tile
 constexpr int kMaxK = 4096;
 constexpr int kMaxTiles = kMaxK / kBI;
 constexpr int kOTW = kDv / 32 / 4;       // 32-column O tiles per wave
@@ -75,8 +75,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kP0 = 16.f;              // P factor of the first pass
 constexpr float kPMax = 448.f;           // P factor of the exact-max pass
 constexpr float kHeadroom = 4.8f;        // < log2(448 / kP0)
-static_assert(kBI * kCPR % kThreads == 0, "staging");
-static_assert(kRS % 64 == 32, "row stride: odd number of 32-byte units");
+static_assert(kUnits % 4 == 0, "units per wave");
+static_assert(kBI == 64, "a 64-lane load fills one unit of a tile");
 
 __device__ __forceinline__ f32x16 mfma_f8_32x32x64(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -98,12 +98,62 @@ __device__ __forceinline__ void qk_drain(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
-// MFMA row r (0..31) of a 32-row half reads LDS row pi(r) of that half.  A
-// lane (h, g) of the C layout holds rows 8i + 4g + j; with pi its rows for
-// i in {2p, 2p+1} are 8 rows distinct mod 8 (one transposing read without
-// bank conflicts), and MFMA rows 8m..8m+7 stay 8 LDS rows distinct mod 8
-// (the QK^T operand read).
-__device__ __forceinline__ int pi_row(int r) { return r ^ ((r >> 1) & 4); }
+// LDS tile layout, unit-major: the 16-byte unit u of tile row r is at
+// u * kUS + 16 r.  A 64-lane direct load then fills one unit of all 64 rows
+// (lane l: row l), so a lane's global address is its row's address plus
+// 16 u.  The QK^T operand read (32 consecutive rows of one unit) is
+// conflict-free, and the 64-byte pad after each unit puts the two 16-column
+// halves of a transposing read (units u and u+1, 8 rows x 16 bytes each)
+// on different banks.
+
+// Workgroup barriers without the release fence of __syncthreads(), which
+// waits for every outstanding global load, the direct-to-LDS loads of a
+// tile still in flight included.  bar_lds(): this wave's LDS accesses are
+// done (its LDS writes are visible to the workgroup after the barrier);
+// bar_all(): its global loads (direct-to-LDS ones included) too.  The
+// memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void bar_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void bar_all() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4:
+// lane l's bytes go to LDS address M0 + 16 l).  Written as inline asm so
+// that the compiler, which cannot tell which LDS buffer such a load writes,
+// does not make every later LDS read wait for it; the waits these loads
+// need are explicit (bar_all()).  The compiler's own vmcnt waits stay
+// correct: loads it does not know of only make them more conservative.
+// One wait state separates the M0 write from the load that reads it.
+// OFF is the instruction's offset, added to both the global and the LDS
+// address.
+template <int OFF>
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               :
+               : "v"(src), "s"(lds_addr), "i"(OFF)
+               : "memory", "m0");
+}
+
+// f(IC<0>{}), ..., f(IC<N-1>{}): a loop whose index is a compile-time
+// constant in the body (register arrays indexed by it stay in registers
+// however large the body grows).
+template <class F, int... Ns>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Ns...>) {
+  (f(IC<Ns>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+struct f32x8_pair {
+  float4 a, b;
+};
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
@@ -132,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   __shared__ int sList[kMaxTiles], sFirst[kMaxTiles];
   // per tile row: (kv_scale, score bias): (scale, 0) or (0, -inf) for an invalid slot
   __shared__ __align__(16) float2 sSB[3][kBI];
-  __shared__ __align__(16) i32x8 sP[2][NHT][kWave];  // P^T fragments, double-buffered
+  // P^T fragments of tile i in buffer i % 2: [head tile][row half][lane]
+  __shared__ __align__(16) i32x4 sP[2][NHT][2][kWave];
   __shared__ float sMx[TS][HQ], sLs[TS][HQ], sMf[HQ];
   __shared__ float sRed[kThreads / kWave];
   __shared__ int sNvt, sFlag;
@@ -185,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
 #pragma unroll
   for (int w = 0; w < kThreads / kWave; ++w) sigma = fmaxf(sigma, sRed[w]);
   const float inv_sigma = sigma > 0.f ? 1.f / sigma : 1.f;
-  // per tile: the first valid index (invalid slots gather that row)
+  // per tile: the first valid index; the invalid slots of a tile with one
+  // are rewritten to ~first (negative: still invalid, and the row they
+  // gather, finite data whose probability is exactly 0, is v ^ (v >> 31))
   for (int t = tid; t < ntiles; t += kThreads) {
     int first = -1;
     for (int r = kBI - 1; r >= 0; --r) {
@@ -193,6 +246,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
       first = v >= 0 ? v : first;
     }
     sFirst[t] = first;
+    if (first >= 0)
+      for (int r = 0; r < kBI; ++r)
+        if (sIdx[t * kBI + r] < 0) sIdx[t * kBI + r] = ~first;
   }
   __syncthreads();
   if (wave == 0) {
@@ -211,50 +267,56 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   const int nvt = sNvt;
 
   // ---- staging: direct global -> LDS loads ---------------------------------
-  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS address M0 +
-  // 16 l (the instruction offset, 0 here, would be added to both
-  // addresses).  A tile buffer (64 rows x 608 bytes) is 38 blocks of 1 KiB;
-  // wave w fills blocks w, w+4, ...  A lane whose 16 bytes fall in a row's
-  // padding loads that row's first chunk (unused).  No VGPRs hold the tile
-  // on its way, and the loads complete while the other phase runs; the
-  // wait for them comes before the barrier that publishes the tile.
+  // A tile buffer is 36 units; wave w fills units w, w+4, ... (9 each), one
+  // 64-lane direct load per unit with lane l loading row l.  No VGPRs hold
+  // the tile on its way; the wait for the loads comes right before the
+  // barrier that publishes the tile.
   float2 psb = float2{0.f, -INFINITY};
   const uint8_t* kvb = kv + (size_t)b * N * kDqk;
-  constexpr int kBlocks = kTile / 1024;
-  static_assert(kTile % 1024 == 0, "tile blocks");
-  auto issue = [&](int tile, int buf) {
-    const int* ti = sIdx + tile * kBI;
-    const int first = sFirst[tile];
+  constexpr int kUPW = kUnits / 4;  // units per wave
+  auto issue_sb = [&](int tile) __attribute__((always_inline)) {
     if (tid < kBI) {
-      const int row = ti[tid];
+      const int row = sIdx[tile * kBI + tid];
       psb = row >= 0 ? float2{ksb[row], 0.f} : float2{0.f, -INFINITY};
     }
-    uint8_t* dst = &sKV[buf][0];
-#pragma unroll
-    for (int k = 0; k < (kBlocks + 3) / 4; ++k) {
-      const int bi = wave + 4 * k;
-      if (bi < kBlocks) {  // uniform over the wave
-        const int p16 = bi * 64 + lane;  // 16-byte unit of the tile buffer
-        const int r = p16 / (kRS / 16), u = p16 % (kRS / 16);
-        int row = ti[r];
-        row = row >= 0 ? row : first;
-        const uint8_t* src = kvb + (size_t)row * kDqk + (u < kCPR ? u * 16 : 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(dst + bi * 1024),
-                                         16, 0, 0);
-      }
+  };
+  // LDS address of tile buffer 0 (the others follow at kTile-byte steps)
+  const uint32_t kv_lds =
+      (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(&sKV[0][0]);
+  // this lane's row of a tile, at this wave's first unit (invalid slots:
+  // the tile's first valid row)
+  auto row_src = [&](int tile) __attribute__((always_inline)) {
+    const int v = sIdx[tile * kBI + lane];
+    return kvb + (size_t)(v ^ (v >> 31)) * kDqk + 16 * wave;
+  };
+  // unit wave + 4k of the tile whose row addresses are in src
+  auto issue_unit = [&](const uint8_t* src, int k, int buf) __attribute__((always_inline)) {
+    const uint32_t lds = kv_lds + buf * kTile + wave * kUS;
+    switch (k) {  // the global offset 64 k is an immediate (added to the LDS address too)
+#define DSA_F8_UNIT(K) \
+  case K: lds_dma16<64 * K>(src, __builtin_amdgcn_readfirstlane(lds + K * (4 * kUS - 64))); break;
+      DSA_F8_UNIT(0) DSA_F8_UNIT(1) DSA_F8_UNIT(2) DSA_F8_UNIT(3) DSA_F8_UNIT(4)
+      DSA_F8_UNIT(5) DSA_F8_UNIT(6) DSA_F8_UNIT(7) DSA_F8_UNIT(8)
+#undef DSA_F8_UNIT
+      default: break;
     }
   };
-  auto commit = [&](int buf) {
+  auto issue_all = [&](int tile, int buf) __attribute__((always_inline)) {
+    issue_sb(tile);
+    const uint8_t* src = row_src(tile);
+#pragma unroll
+    for (int k = 0; k < kUPW; ++k) issue_unit(src, k, buf);
+  };
+  auto commit = [&](int buf) __attribute__((always_inline)) {
     if (tid < kBI) sSB[buf][tid] = psb;
   };
   // vmcnt(0): every global load of this wave, the direct-to-LDS ones
   // included, has landed
-  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0f70); };
+  auto wait_loads = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0f70); };
 
   // ---- per-tile pieces --------------------------------------------------------
   f32x16 oacc[NHT][kOTW];
-  auto zero_o = [&]() {
+  auto zero_o = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int oh = 0; oh < NHT; ++oh)
 #pragma unroll
@@ -268,145 +330,184 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   float xmax = -INFINITY;  // largest x - m seen (first pass: overflow check)
   f32x16 sacc[NT];         // S^T of the tile in flight
 
-  // QK^T of a tile: row half tau's MFMA row r reads LDS row 32 tau + pi(r).
-  // The A fragments of k-step s+1 are read before the MFMAs of step s, and
-  // a scheduling barrier keeps the compiler from hoisting every read (which
-  // would cost registers).
-  auto qk = [&](const uint8_t* sK) {
+  // QK^T operand: lane (r, g) of row half tau reads row 32 tau + r, logical
+  // units 4s + 2g and 4s + 2g + 1 of k-step s
+  const int aoff0 = (2 * g) * kUS + 16 * (32 * tau0 + hl);
+  const int aoff1 = aoff0 + kUS;
+  auto lda = [&](const uint8_t* sK, int s, int u) __attribute__((always_inline)) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(sK + aoff0 + 512 * u + 4 * kUS * s);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(sK + aoff1 + 512 * u + 4 * kUS * s);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // QK^T of a tile, one k-step at a time (the next step's operands are read
+  // before this step's MFMAs; a scheduling barrier between steps keeps the
+  // compiler from hoisting every read).  `extra(s)` runs after the MFMAs of
+  // step s: the issue of the next tile's loads, spread over the k-steps.
+  auto qk = [&](const uint8_t* sK, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[u][e] = 0.f;
-    const uint8_t* abase = sK + (32 * tau0 + pi_row(hl)) * kRS + 32 * g;
     i32x8 a[2][NT];
-    auto ld = [&](int s) {
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const uint8_t* arow = abase + 32 * u * kRS + 64 * s;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(arow);
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + 16);
-        a[s & 1][u] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int u = 0; u < NT; ++u) a[0][u] = lda(sK, 0, u);
+    static_for<kKS>([&](auto ss) __attribute__((always_inline)) {
+      constexpr int s = decltype(ss)::value;
+      if constexpr (s + 1 < kKS) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) a[(s + 1) & 1][u] = lda(sK, s + 1, u);
       }
-    };
-    ld(0);
-#pragma unroll
-    for (int s = 0; s < kKS; ++s) {
-      if (s + 1 < kKS) ld(s + 1);
 #pragma unroll
       for (int u = 0; u < NT; ++u) qk_mfma(sacc[u], a[s & 1][u], qf[s]);
+      extra(s);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
 #pragma unroll
     for (int u = 0; u < NT; ++u) qk_drain(sacc[u]);
   };
-  // C registers 4i..4i+3 of row half tau hold LDS rows 32 tau + pi(8i + 4g)
-  // + 0..3, which are consecutive: their (scale, bias) pairs are two
-  // 16-byte reads.
-  auto rowsb = [&](const float2* sb, int tau, int i, float2 (&v)[4]) {
-    const float4* p4 = reinterpret_cast<const float4*>(sb + 32 * tau + pi_row(8 * i + 4 * g));
-    const float4 a = p4[0], c = p4[1];
-    v[0] = float2{a.x, a.y};
-    v[1] = float2{a.z, a.w};
-    v[2] = float2{c.x, c.y};
-    v[3] = float2{c.z, c.w};
+  auto no_extra = [](int) __attribute__((always_inline)) {};
+  // C registers 4i..4i+3 of row half tau hold rows 32 tau + 8i + 4g + 0..3:
+  // their (scale, bias) pairs are two 16-byte reads
+  auto rowsb = [&](const float2* sb, int tau, int i) __attribute__((always_inline)) {
+    const float4* p4 = reinterpret_cast<const float4*>(sb + 32 * tau + 8 * i + 4 * g);
+    return f32x8_pair{p4[0], p4[1]};
   };
   // largest x of the tile in flight for this lane's head (masked: -inf)
-  auto tile_max = [&](const float2* sb) {
+  auto tile_max = [&](const float2* sb) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float2 v[4];
-        rowsb(sb, tau0 + u, i, v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaf(sacc[u][4 * i + j], qsl * v[j].x, v[j].y));
+        const f32x8_pair v = rowsb(sb, tau0 + u, i);
+        mx = fmaxf(mx, fmaf(sacc[u][4 * i + 0], qsl * v.a.x, v.a.y));
+        mx = fmaxf(mx, fmaf(sacc[u][4 * i + 1], qsl * v.a.z, v.a.w));
+        mx = fmaxf(mx, fmaf(sacc[u][4 * i + 2], qsl * v.b.x, v.b.y));
+        mx = fmaxf(mx, fmaf(sacc[u][4 * i + 3], qsl * v.b.z, v.b.w));
       }
     return fmaxf(mx, wave_xor(mx, 32));
   };
-  // softmax of the tile in flight: P = 2^(x - m) * kv_scale * pf as e4m3,
-  // to this wave's bytes of the P^T fragments in dst
-  auto softmax = [&](const float2* sb, i32x8* dst, float pf) {
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      int pk[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float2 v[4];
-        rowsb(sb, tau0 + u, i, v);
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float t = fmaf(sacc[u][4 * i + j], qsl * v[j].x, v[j].y) - m;
-          xmax = fmaxf(xmax, t);
-          const float e = fast_exp2(t);
-          lsum += e;
-          p[j] = e * (v[j].x * pf);
-        }
-        pk[i] = pack_fp8x4(p[0], p[1], p[2], p[3]);
-      }
-      // P^T bytes 16 tau + 4i + j of lane (h, g) <- C register 4i + j
-      *reinterpret_cast<i32x4*>(reinterpret_cast<int*>(&dst[qht * kWave + lane]) +
-                                4 * (tau0 + u)) = i32x4{pk[0], pk[1], pk[2], pk[3]};
-    }
-  };
 
-  // V^T A-fragment of output column tile t: slot 8q + r of lane half g is LDS
-  // row 32(q>>1) + pi(8(2(q&1) + (r>>2)) + 4g + (r&3)), r = the row the
-  // lane pair (2r, 2r+1) of each 16-lane group addresses.
-  const int l16 = lane & 15, trr = l16 >> 1;
-  const int vcol = c0 + 16 * ((lane >> 4) & 1) + 8 * (l16 & 1);
-  int voff[4];
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq)
-    voff[qq] = (32 * (qq >> 1) + pi_row(8 * (2 * (qq & 1) + (trr >> 2)) + 4 * g + (trr & 3))) * kRS +
-               vcol;
-  auto vfrag = [&](const uint8_t* sK, int t) {
-    const i32x2 r0 = lds_read_tr8(sK + voff[0] + 32 * t);
-    const i32x2 r1 = lds_read_tr8(sK + voff[1] + 32 * t);
-    const i32x2 r2 = lds_read_tr8(sK + voff[2] + 32 * t);
-    const i32x2 r3 = lds_read_tr8(sK + voff[3] + 32 * t);
+  // V^T A-fragment of output column tile t: slot 8q + r of lane half g is
+  // row 32(q>>1) + 8(2(q&1) + (r>>2)) + 4g + (r&3), r = the row the lane
+  // pair (2r, 2r+1) of each 16-lane group addresses; the lane's 8 bytes are
+  // logical unit c0/16 + 2t + ch, half l16 & 1.
+  const int l16 = lane & 15, trr = l16 >> 1, ch = (lane >> 4) & 1;
+  int voff;  // row rr of read 0 at unit c0/16 + ch; reads q add 16 rows, tile t 2 units
+  {
+    const int rr = 8 * (trr >> 2) + 4 * g + (trr & 3);
+    voff = (c0 / 16 + ch) * kUS + 16 * rr + 8 * (l16 & 1);
+  }
+  auto vfrag = [&](const uint8_t* sK, int t) __attribute__((always_inline)) {
+    const uint8_t* vp = sK + voff + 2 * kUS * t;
+    const i32x2 r0 = lds_read_tr8(vp);
+    const i32x2 r1 = lds_read_tr8(vp + 16 * 16);
+    const i32x2 r2 = lds_read_tr8(vp + 16 * 32);
+    const i32x2 r3 = lds_read_tr8(vp + 16 * 48);
     return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   };
-  auto pv = [&](const uint8_t* sK, const i32x8* sPb) {
+
+  // Phase 1 of an iteration: PV of the previous tile (WITH_PV) interleaved
+  // with the softmax of the tile in flight, EPM softmax elements after each
+  // MFMA, so that the VALU work issues while the MFMAs run.  P = 2^(x - m) *
+  // kv_scale * pf goes to this wave's halves of the P^T fragments in dst.
+  constexpr int NM = NHT * kOTW;     // PV MFMAs per wave and tile
+  constexpr int NE = NT * 16;        // softmax elements per lane and tile
+  constexpr int EPM = NE / NM;       // elements per MFMA
+  static_assert(NE % NM == 0 && 4 % EPM == 0, "interleave");
+  // PV runs over pairs of head tiles: the two P fragments of a pair stay in
+  // registers for its kOTW column tiles (the V fragments are read once per
+  // pair), which keeps 16 VGPRs of P live instead of 32.
+  constexpr int OHG = NHT >= 2 ? 2 : 1;  // head tiles per pair
+  constexpr int NPAIR = NM / OHG;        // (pair, column tile) steps
+  auto phase1 = [&](auto with_pv, const uint8_t* sKp, i32x4 (*sPp)[2][kWave],
+                    const float2* sb, i32x4 (*sPc)[2][kWave], float pf) {
+    constexpr bool WPV = decltype(with_pv)::value;
+    i32x8 pb[OHG];
+    i32x8 va[2];
+    auto load_pb = [&](int grp) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < OHG; ++k) {
+        const i32x4 lo = sPp[grp * OHG + k][0][lane], hi = sPp[grp * OHG + k][1][lane];
+        pb[k] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+    if constexpr (WPV) {
+      load_pb(0);
+      va[0] = vfrag(sKp, 0);
+    }
+    f32x8_pair sbv[2];
+    sbv[0] = rowsb(sb, tau0, 0);
+    float p[4];
+    int pk[4];
+    static_for<NM>([&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value;
+      if constexpr (WPV) {
+        constexpr int st = n / OHG, k = n % OHG;  // step (pair, column tile)
+        constexpr int grp = st / kOTW, t = st % kOTW;
+        if constexpr (k == 0 && st + 1 < NPAIR) va[(st + 1) & 1] = vfrag(sKp, (st + 1) % kOTW);
+        oacc[grp * OHG + k][t] = mfma_f8_32x32x64(va[st & 1], pb[k], oacc[grp * OHG + k][t]);
+        if constexpr (k == OHG - 1 && t == kOTW - 1 && grp + 1 < NHT / OHG) load_pb(grp + 1);
+      }
+      static_for<EPM>([&](auto kk) __attribute__((always_inline)) {
+        constexpr int e = n * EPM + decltype(kk)::value, gi = e / 4, j = e % 4, u = gi / 4,
+                      i = gi % 4;
+        if constexpr (j == 0 && gi + 1 < NT * 4)
+          sbv[(gi + 1) & 1] = rowsb(sb, tau0 + (gi + 1) / 4, (gi + 1) % 4);
+        const f32x8_pair& v = sbv[gi & 1];
+        const float ks = j == 0 ? v.a.x : j == 1 ? v.a.z : j == 2 ? v.b.x : v.b.z;
+        const float bias = j == 0 ? v.a.y : j == 1 ? v.a.w : j == 2 ? v.b.y : v.b.w;
+        const float tt = fmaf(sacc[u][4 * i + j], qsl * ks, bias) - m;
+        xmax = fmaxf(xmax, tt);
+        const float ex = fast_exp2(tt);
+        lsum += ex;
+        p[j] = ex * (ks * pf);
+        if constexpr (j == 3) {
+          pk[i] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+          if constexpr (i == 3) sPc[qht][tau0 + u][lane] = i32x4{pk[0], pk[1], pk[2], pk[3]};
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // PV alone (the last tile)
+  auto pv_only = [&](const uint8_t* sKp, i32x4 (*sPp)[2][kWave]) {
     i32x8 pb[NHT];
 #pragma unroll
-    for (int oh = 0; oh < NHT; ++oh) pb[oh] = sPb[oh * kWave + lane];
-    i32x8 va[2];
-    va[0] = vfrag(sK, 0);
+    for (int oh = 0; oh < NHT; ++oh) {
+      const i32x4 lo = sPp[oh][0][lane], hi = sPp[oh][1][lane];
+      pb[oh] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
 #pragma unroll
     for (int t = 0; t < kOTW; ++t) {
-      if (t + 1 < kOTW) va[(t + 1) & 1] = vfrag(sK, t + 1);
+      const i32x8 va = vfrag(sKp, t);
 #pragma unroll
-      for (int oh = 0; oh < NHT; ++oh)
-        oacc[oh][t] = mfma_f8_32x32x64(va[t & 1], pb[oh], oacc[oh][t]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int oh = 0; oh < NHT; ++oh) oacc[oh][t] = mfma_f8_32x32x64(va, pb[oh], oacc[oh][t]);
     }
   };
 
   // Pipelined pass (mode 0: reference = the first tile's max, P factor 16;
   // mode 2: the exact max, P factor 448).  Iteration it: | PV of tile it-1
-  // beside the softmax of tile it | QK^T of tile it+1 beside the LDS store
-  // of tile it+2 (gathered into VGPRs one iteration earlier) and the gather
-  // of tile it+3 |.  Three LDS tile buffers: tile i lives in buffer i % 3
-  // from its store (iteration i-2) to its PV (iteration i+1); the buffer
-  // tile it+2 is stored into held tile it-1, whose PV ends before the
-  // barrier that opens the second half.
-  auto pipelined = [&](int mode) {
-    const float pf = (mode == 2 ? kPMax : kP0) * inv_sigma;
+  // beside the softmax of tile it | QK^T of tile it+1 beside the issue of
+  // tile it+2's loads |.  Three LDS tile buffers: tile i lives in buffer
+  // i % 3 from its load (issued in iteration i-2) to its PV (iteration
+  // i+1); the buffer tile it+2 goes to held tile it-1, whose PV ends before
+  // the barrier that opens the second half.
+  auto pipelined = [&]() __attribute__((always_inline)) {
+    const float pf = kP0 * inv_sigma;
     if (nvt == 0) return;
     __syncthreads();  // every wave is past its previous use of the buffers
-    issue(sList[0], 0);
+    issue_all(sList[0], 0);
     wait_loads();
     commit(0);
     if (nvt > 1) {
-      issue(sList[1], 1);
+      issue_all(sList[1], 1);
       wait_loads();
       commit(1);
     }
     __syncthreads();
-    qk(sKV[0]);
-    if (mode == 0) {
+    qk(sKV[0], no_extra);
+    {
       float mx = tile_max(sSB[0]);
       if constexpr (TS == 2) {
         if (g == 0) sMx[tau0][hq] = mx;
@@ -415,38 +516,47 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
       }
       m = mx;  // the first tile holds a valid index: finite
     }
-    int bc = 0;  // buffer of tile it: it % 3
-    auto step = [&](int it, auto later) {
+    // iteration it with tile it in buffer bc = it % 3 (its P goes to P
+    // buffer bc as well)
+    int bc = 0;
+    auto step = [&](int it, auto later) __attribute__((always_inline)) {
       const int bp = bc == 0 ? 2 : bc - 1, bn = bc == 2 ? 0 : bc + 1;
-      __syncthreads();  // P of tile it-1 visible
-      if constexpr (decltype(later)::value) pv(sKV[bp], &sP[(it - 1) & 1][0][0]);
-      softmax(sSB[bc], &sP[it & 1][0][0], pf);
+      bar_lds();  // P of tile it-1 visible (tile it+2's loads stay in flight)
+      phase1(later, sKV[bp], sP[(it - 1) & 1], sSB[bc], sP[it & 1], pf);
       if constexpr (decltype(later)::value) {
         if (it + 1 < nvt) commit(bn);  // row scales of tile it+1, loaded in the last iteration
       }
-      wait_loads();     // tile it+1 has landed in LDS
-      __syncthreads();  // P of tile it and tile it+1 visible; tile it-1's buffer free
-      qk(sKV[bn]);      // tile it+1 (past the last tile: unused)
-      if (it + 2 < nvt) issue(sList[it + 2], bp);
+      bar_all();  // tile it+1 landed; P of tile it visible; tile it-1's buffer free
+      if (it + 2 < nvt) {
+        const int tile = sList[it + 2];
+        issue_sb(tile);
+        const uint8_t* src = row_src(tile);
+        qk(sKV[bn], [&](int s) __attribute__((always_inline)) {
+          if (s < kUPW) issue_unit(src, s, bp);
+        });
+      } else {
+        qk(sKV[bn], no_extra);  // tile it+1 (past the last tile: unused)
+      }
       bc = bn;
     };
     step(0, std::false_type{});
 #pragma unroll 1
     for (int it = 1; it < nvt; ++it) step(it, std::true_type{});
-    __syncthreads();  // P of the last tile visible
-    pv(sKV[bc == 0 ? 2 : bc - 1], &sP[(nvt - 1) & 1][0][0]);
+    bar_all();  // P of the last tile visible
+    const int bl = bc == 0 ? 2 : bc - 1;
+    pv_only(sKV[bl], sP[(nvt - 1) & 1]);
   };
   // Max-only pass: the exact max of each head (one tile at a time).
-  auto prepass = [&]() {
+  auto prepass = [&]() __attribute__((always_inline)) {
     m = -INFINITY;
 #pragma unroll 1
     for (int it = 0; it < nvt; ++it) {
       __syncthreads();  // the previous tile's QK^T is done
-      issue(sList[it], 0);
+      issue_all(sList[it], 0);
       wait_loads();
       commit(0);
       __syncthreads();
-      qk(sKV[0]);
+      qk(sKV[0], no_extra);
       m = fmaxf(m, tile_max(sSB[0]));
     }
     if constexpr (TS == 2) {
@@ -456,8 +566,25 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     }
   };
 
+  // Pass at the exact max (after a restart): one tile at a time.
+  auto exact_pass = [&]() __attribute__((always_inline)) {
+    const float pf = kPMax * inv_sigma;
+#pragma unroll 1
+    for (int it = 0; it < nvt; ++it) {
+      __syncthreads();  // the previous tile's PV is done
+      issue_all(sList[it], 0);
+      wait_loads();
+      commit(0);
+      __syncthreads();
+      qk(sKV[0], no_extra);
+      phase1(std::false_type{}, sKV[0], sP[0], sSB[0], sP[1], pf);
+      __syncthreads();
+      pv_only(sKV[0], sP[1]);
+    }
+  };
+
   int mode = 0;
-  pipelined(0);
+  pipelined();
   if (__ballot(xmax > kHeadroom) != 0ull && lane == 0) sFlag = 1;
   __syncthreads();
   if (sFlag != 0) {
@@ -467,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     __syncthreads();  // every wave is past its last tile
     prepass();
     mode = 2;
-    pipelined(2);
+    exact_pass();
   }
 
   // ---- sink, normalise, store -------------------------------------------------
@@ -518,8 +645,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     // bf16 O through LDS (the KV buffers, free now) in passes of 64 heads so
     // that each head row of o is written whole with 16-byte lanes
     constexpr int OS = kDv + 8;  // row stride (elements): 16-byte aligned rows
-    constexpr int ORP = 64;      // head rows per pass
-    static_assert(ORP * OS * 2 <= (int)sizeof(sKV), "O staging");
+    constexpr int ORP = 32;      // head rows per pass
+    static_assert(ORP * OS * 2 <= kTile, "O staging");
     uint16_t* so = reinterpret_cast<uint16_t*>(&sKV[0][0]);
 #pragma unroll
     for (int pass = 0; pass < HQ / ORP; ++pass) {
