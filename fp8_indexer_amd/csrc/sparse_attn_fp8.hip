@@ -217,39 +217,42 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     }
   }
   const float qsl = (q_scale ? q_scale[(size_t)rtok * HQ + hq] : 1.f) * scale_log2;
-  // indices (sanitised: -1 = invalid) and the largest kv_scale among them
+  // Indices: wave w takes tiles w, w+4, ... (a tile is 64 indices, one per
+  // lane), all loaded before any is used.  Invalid indices (-1 or outside
+  // [0, N)) become ~first, first = the tile's first valid index (negative:
+  // still invalid; the row such a slot gathers, finite data whose
+  // probability is exactly 0, is v ^ (v >> 31)).  sigma = the largest
+  // kv_scale of the valid indices.
   const int* ridx = idx + (size_t)rtok * K + kbeg;
   const float* ksb = kv_scale + (size_t)b * N;
-  float smax = 0.f;
-  for (int p = tid; p < nidx; p += kThreads) {
-    int v = p < klen ? ridx[p] : -1;
-    v = (v >= 0 && v < N) ? v : -1;
-    sIdx[p] = v;
-    if (v >= 0) smax = fmaxf(smax, ksb[v]);
+  constexpr int kTPW = kMaxTiles / 4;  // tiles per wave at most
+  int vv[kTPW];
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int p = (wave + 4 * j) * kBI + lane;
+    vv[j] = p < klen ? ridx[p] : -1;
   }
+  float smax = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int t = wave + 4 * j;
+    int v = vv[j];
+    v = (v >= 0 && v < N) ? v : -1;
+    vv[j] = v;
+    if (t < ntiles) {  // uniform over the wave
+      const uint64_t mk = __ballot(v >= 0);
+      const int first = mk ? __shfl(v, (int)__builtin_ctzll(mk), kWave) : -1;
+      sIdx[t * kBI + lane] = v >= 0 ? v : (first >= 0 ? ~first : -1);
+      if (lane == 0) sFirst[t] = first;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j)
+    if (vv[j] >= 0) smax = fmaxf(smax, ksb[vv[j]]);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) smax = fmaxf(smax, __shfl_xor(smax, sh, kWave));
   if (lane == 0) sRed[wave] = smax;
   if (tid == 0) sFlag = 0;
-  __syncthreads();
-  float sigma = 0.f;
-#pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) sigma = fmaxf(sigma, sRed[w]);
-  const float inv_sigma = sigma > 0.f ? 1.f / sigma : 1.f;
-  // per tile: the first valid index; the invalid slots of a tile with one
-  // are rewritten to ~first (negative: still invalid, and the row they
-  // gather, finite data whose probability is exactly 0, is v ^ (v >> 31))
-  for (int t = tid; t < ntiles; t += kThreads) {
-    int first = -1;
-    for (int r = kBI - 1; r >= 0; --r) {
-      const int v = sIdx[t * kBI + r];
-      first = v >= 0 ? v : first;
-    }
-    sFirst[t] = first;
-    if (first >= 0)
-      for (int r = 0; r < kBI; ++r)
-        if (sIdx[t * kBI + r] < 0) sIdx[t * kBI + r] = ~first;
-  }
   __syncthreads();
   if (wave == 0) {
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -264,6 +267,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     if (lane == 0) sNvt = base;
   }
   __syncthreads();
+  float sigma = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) sigma = fmaxf(sigma, sRed[w]);
+  const float inv_sigma = sigma > 0.f ? 1.f / sigma : 1.f;
   const int nvt = sNvt;
 
   // ---- staging: direct global -> LDS loads ---------------------------------
@@ -274,12 +281,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   float2 psb = float2{0.f, -INFINITY};
   const uint8_t* kvb = kv + (size_t)b * N * kDqk;
   constexpr int kUPW = kUnits / 4;  // units per wave
-  auto issue_sb = [&](int tile) __attribute__((always_inline)) {
+  auto issue_sb_to = [&](int tile, float2& dst) __attribute__((always_inline)) {
     if (tid < kBI) {
       const int row = sIdx[tile * kBI + tid];
-      psb = row >= 0 ? float2{ksb[row], 0.f} : float2{0.f, -INFINITY};
+      dst = row >= 0 ? float2{ksb[row], 0.f} : float2{0.f, -INFINITY};
     }
   };
+  auto issue_sb = [&](int tile) __attribute__((always_inline)) { issue_sb_to(tile, psb); };
   // LDS address of tile buffer 0 (the others follow at kTile-byte steps)
   const uint32_t kv_lds =
       (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(&sKV[0][0]);
@@ -497,14 +505,18 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     const float pf = kP0 * inv_sigma;
     if (nvt == 0) return;
     __syncthreads();  // every wave is past its previous use of the buffers
+    // tiles 0 and 1 together: one wait
+    float2 psb1 = float2{0.f, -INFINITY};
     issue_all(sList[0], 0);
+    if (nvt > 1) {
+      issue_sb_to(sList[1], psb1);
+      const uint8_t* src = row_src(sList[1]);
+#pragma unroll
+      for (int k = 0; k < kUPW; ++k) issue_unit(src, k, 1);
+    }
     wait_loads();
     commit(0);
-    if (nvt > 1) {
-      issue_all(sList[1], 1);
-      wait_loads();
-      commit(1);
-    }
+    if (tid < kBI) sSB[1][tid] = psb1;
     __syncthreads();
     qk(sKV[0], no_extra);
     {
@@ -645,8 +657,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     // bf16 O through LDS (the KV buffers, free now) in passes of 64 heads so
     // that each head row of o is written whole with 16-byte lanes
     constexpr int OS = kDv + 8;  // row stride (elements): 16-byte aligned rows
-    constexpr int ORP = 32;      // head rows per pass
-    static_assert(ORP * OS * 2 <= kTile, "O staging");
+    constexpr int ORP = 64;      // head rows per pass (tile buffers 0 and 1)
+    static_assert(ORP * OS * 2 <= 2 * kTile, "O staging");
     uint16_t* so = reinterpret_cast<uint16_t*>(&sKV[0][0]);
 #pragma unroll
     for (int pass = 0; pass < HQ / ORP; ++pass) {
