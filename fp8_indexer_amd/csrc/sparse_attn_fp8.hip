@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   // PV runs over pairs of head tiles: the two P fragments of a pair stay in
   // registers for its kOTW column tiles (the V fragments are read once per
   // pair), which keeps 16 VGPRs of P live instead of 32.
-  constexpr int OHG = NHT >= 2 ? 2 : 1;  // head tiles per pair
+  constexpr int OHG = NHT;  // head tiles per pair
   constexpr int NPAIR = NM / OHG;        // (pair, column tile) steps
   auto phase1 = [&](auto with_pv, const uint8_t* sKp, i32x4 (*sPp)[2][kWave],
                     const float2* sb, i32x4 (*sPc)[2][kWave], float pf) {
