@@ -13,7 +13,9 @@ against the 2.5 PFLOP/s dense bf16 MFMA peak.  `stages` also gives each
 stage timed with L2 and the MALL flushed before every step, the dsa_prefill
 entry point warm and flushed, the indexer + top-k without a logits buffer
 (dsa_indexer_topk: time, and peak device memory against the unfused way),
-and the attention backward at the same shapes (bf16 kv).  `cpu_baseline`
+the attention backward at the same shapes (bf16 kv), and the full-FP8
+attention (dsa_sparse_attn_fwd_fp8: e4m3 q and KV quantised from the same
+draws, the same top-k indices; against the 5.0 PFLOP/s fp8 peak).  `cpu_baseline`
 times the CPU oracle (indexer -> top-k -> attention), stage by stage, on a
 bounded sample of rows.
 
@@ -165,6 +167,8 @@ def main():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="steps timed with L2/MALL flushed before each (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--fp8-attn-reps", type=int, default=5,
+                    help="timed runs of the full-FP8 attention (0: skip)")
     ap.add_argument("--backward-reps", type=int, default=3,
                     help="timed calls of the attention backward (0 = skip)")
     ap.add_argument("--workload", default="prefill_4096",
@@ -350,6 +354,37 @@ def main():
                "algorithmic_tflop": bwd_flops / 1e12, "reps": args.backward_reps}
         del dq, dkv, gO
 
+    # full-FP8 attention (e4m3 q and KV, fp8 MFMA for both products) on the
+    # same top-k indices, with q and kv quantised from the same draws
+    f8 = None
+    if dsa.attn_fp8_supported(wl.Hq, wl.Dqk, wl.Dv) and args.fp8_attn_reps > 0:
+        eprint("[bench] full-FP8 attention")
+        wl8 = wl.with_(name=wl.name + "_fp8attn", q_fp8=True, kv_fp8=True)
+        x8 = W.make_inputs(wl8, parts=("attn",))
+        g8 = {k: x8[k].to(dev) for k in ("q", "qa_scale", "kv", "kv_scale")}
+        del x8
+        o8 = torch.empty_like(o)
+        f8args = (g8["q"], g8["qa_scale"], g8["kv"], g8["kv_scale"], g["sink"], idx, wl.sm_scale,
+                  wl.Dv)
+        t_end = time.time() + 0.3  # warm, like the other stages
+        while time.time() < t_end:
+            dsa.sparse_attn_fwd_fp8(*f8args, out=o8)
+            torch.cuda.synchronize()
+        ft = []
+        for _ in range(args.fp8_attn_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsa.sparse_attn_fwd_fp8(*f8args, out=o8)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ft.append(e0.elapsed_time(e1))
+        ms_f8 = float(np.median(ft))
+        f8_flops = work_counts(wl, x["ks"], x["ke"])["att_flops"]
+        f8 = {"workload": wl8.name, "ms": ms_f8, "tflops": f8_flops / (ms_f8 * 1e-3) / 1e12,
+              "frac_fp8_peak": f8_flops / (ms_f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+              "speedup_vs_bf16_attention": ms_att / ms_f8, "reps": args.fp8_attn_reps}
+        del g8, o8
+
     wc = work_counts(wl, x["ks"], x["ke"])
     tokens = B * M
     att_tflops = wc["att_flops"] / (ms_att * 1e-3) / 1e12
@@ -400,6 +435,7 @@ def main():
                 "peak_bytes": peak_fused, "unfused_peak_bytes": peak_unfused,
                 "logits_buffer_bytes": B * M * N * 4},
             "backward": bwd,
+            "attention_full_fp8": f8,
         },
         "cpu_baseline": None,
     }

@@ -28,7 +28,7 @@ __all__ = ["DSAError", "lib", "version", "indexer_logits", "indexer_topk",
            "indexer_topk_workspace_size", "topk", "sparse_attn_fwd", "sparse_attn_bwd",
            "prefill", "topk_workspace_size", "sparse_attn_workspace_size",
            "prefill_workspace_size", "prefill_noalloc", "sparse_attn_fwd_fp8",
-           "sparse_attn_fp8_workspace_size", "KV_BF16", "KV_FP8_E4M3FN",
+           "sparse_attn_fp8_workspace_size", "attn_fp8_supported", "KV_BF16", "KV_FP8_E4M3FN",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -208,6 +208,14 @@ def sparse_attn_fp8_workspace_size(B, M, Hq, Dqk, Dv, K):
     _check("dsa_sparse_attn_fp8_workspace_size",
            lib().dsa_sparse_attn_fp8_workspace_size(B, M, Hq, Dqk, Dv, K, ctypes.byref(n)))
     return n.value
+
+
+def attn_fp8_supported(Hq, Dqk, Dv):
+    """Whether dsa_sparse_attn_fwd_fp8 supports these head and width sizes
+    (asked of the library: its workspace-size query validates the shape)."""
+    n = ctypes.c_size_t(0)
+    rc = lib().dsa_sparse_attn_fp8_workspace_size(1, 1, Hq, Dqk, Dv, 1, ctypes.byref(n))
+    return rc == 0
 
 
 def indexer_logits(q, q_scale, k, k_scale, weights, ks, ke, logits=None):
