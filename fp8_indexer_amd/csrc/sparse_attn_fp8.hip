@@ -30,15 +30,18 @@
 //    of each gathered row is chosen so that the V^T A-fragment can be read
 //    with gfx950's 8-bit transposing LDS load (ds_read_b64_tr_b8: in each
 //    16-lane group, lanes 2r and 2r+1 give the address of row r's 16 bytes
-//    and lane i receives byte i of all 8 rows).  The row permutation pi
-//    below also keeps both LDS reads free of bank conflicts.  This replaces
-//    the K-major V copy that the TileLang page builds in shared memory.
+//    and lane i receives byte i of all 8 rows; the row order is given at
+//    vfrag below).  This replaces the K-major V copy that the TileLang page
+//    builds in shared memory.
 //  * All 4 waves share P through LDS and split the 512 output columns, so
 //    each V fragment feeds one MFMA per 32-head tile and O (128 heads x 128
 //    columns per wave) fills the AGPRs.
-//  * KV tiles of 64 rows (576 bytes each, row stride 608 bytes) are gathered
-//    into VGPRs while the current tile's QK^T runs and written to the other
-//    LDS buffer after the softmax (double buffering, two barriers per tile).
+//  * KV tiles of 64 gathered rows go straight from global memory to LDS
+//    (one 64-lane direct load per 16-byte unit of the row, lane = row) in
+//    a unit-major layout, three tile buffers deep.  Software pipeline, one
+//    iteration per tile: the PV of tile i-1 interleaved MFMA by MFMA with
+//    the softmax of tile i, then the QK^T of tile i+1 with the loads of
+//    tile i+2 issued between its k-steps; two barriers per iteration.
 //  * Softmax in base 2 with sm_scale*log2(e) and q_scale folded into one
 //    per-head factor.  The exponent reference of each head is the first
 //    tile's max and is never moved, so O is only ever touched by MFMA; P is
