@@ -43,6 +43,7 @@ constexpr int kRT = kRowsPerWave / 16;          // 16-row MFMA tiles per wave
 constexpr int kKT = DSA_IDX_KT;                 // keys per LDS tile (tuning knob)
 constexpr int kXcds = 8;
 constexpr int kMinChunk = 64;   // keys per chunk, at least (one key tile)
+constexpr int kBalBlocks = 1024;  // key-parallel: token blocks of the balanced schedule, at most
 // VALU instructions scheduled after each MFMA of the next sub-tile (tuning knob)
 #ifndef DSA_IDX_VPM
 #define DSA_IDX_VPM 10
@@ -156,12 +157,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   __shared__ __align__(16) uint8_t sK[2][C::TILE_BYTES];
   __shared__ float sKs[2][C::KT];
   __shared__ int sRed[2][kIdxWaves];
+  __shared__ int sCum[KP ? kBalBlocks + 1 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
 
-  // ---- one item: (batch b, token block tb, key chunk) ---------------------
-  auto process = [&](const int b, const int tb, const int chunk) {
+  // ---- one item: (batch b, token block tb, keys [off0, off1) of the
+  // block's window union, counted from its start) -------------------------
+  auto process = [&](const int b, const int tb, const int off0, const int off1) {
   const int t0 = tb * C::TB;
 
   // ---- this wave's tokens: q fragments and effective weights (issued
@@ -226,9 +229,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     kmin = min(kmin, sRed[0][i]);
     kmax = max(kmax, sRed[1][i]);
   }
-  const int c0 = kmin + chunk * chunk_keys;
+  const int c0 = kmin + off0;
   if (kmin >= kmax || c0 >= kmax) return;  // uniform across the workgroup
-  const int c1 = min(kmax, c0 + chunk_keys);
+  const int c1 = min(kmax, kmin + off1);
 
   // windows of the wave (for tile skipping) and of this lane's tokens
   // (token of slot j: (32*g)/H + j), clipped to the chunk so that
@@ -423,11 +426,90 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
   };
 
   if constexpr (KP) {
-    // decode: one item per workgroup, items in id order (chunks of a batch
-    // entry spread over the XCDs)
-    const int per_batch = n_tblocks * n_chunks;
-    const int id = blockIdx.x % per_batch;
-    process(blockIdx.x / per_batch, n_tblocks - 1 - id / n_chunks, id % n_chunks);
+    if (n_chunks > 0) {
+      // one item per workgroup, items in id order (chunks of a batch entry
+      // spread over the XCDs)
+      const int per_batch = n_tblocks * n_chunks;
+      const int id = blockIdx.x % per_batch;
+      const int off = (id % n_chunks) * chunk_keys;
+      process(blockIdx.x / per_batch, n_tblocks - 1 - id / n_chunks, off, off + chunk_keys);
+      return;
+    }
+    // Balanced (n_chunks == 0; at most kBalBlocks token blocks): the window
+    // unions of all blocks, laid end to end, are cut into gridDim.x equal
+    // ranges of whole key tiles, one per workgroup, each processed as the
+    // pieces it covers in every block it spans.  The host cannot size
+    // chunks by the windows (they are in device memory); decode windows
+    // differ by an order of magnitude between batch entries.
+    const int nblk = B * n_tblocks;
+    constexpr int kPer = kBalBlocks / kIdxThreads;  // blocks per thread
+    int len[kPer], tsum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid * kPer + j;
+      int smin = N, emax = 0;
+      if (i < nblk) {
+        const int bb = i / n_tblocks, tb = i % n_tblocks;
+        for (int tl = 0; tl < C::TB; ++tl) {
+          const int t = tb * C::TB + tl;
+          if (t < M) {
+            const int r = bb * M + t;
+            const int s0 = clampi(ks[r], 0, N);
+            const int e0 = clampi(ke[r], s0, N);
+            if (e0 > s0) {
+              smin = min(smin, s0);
+              emax = max(emax, e0);
+            }
+          }
+        }
+      }
+      len[j] = emax > smin ? emax - smin : 0;
+      tsum += len[j];
+    }
+    // exclusive prefix of the block lengths in sCum[0..nblk], sCum[nblk] =
+    // total (lane scan by shuffles, then the wave totals)
+    int incl = tsum;
+#pragma unroll
+    for (int sh = 1; sh < kWave; sh <<= 1) {
+      const int y = __shfl_up(incl, sh, kWave);
+      if (lane >= sh) incl += y;
+    }
+    if (lane == kWave - 1) sRed[0][wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kIdxWaves; ++i) {
+      before += i < wave ? sRed[0][i] : 0;
+      total += sRed[0][i];
+    }
+    int run = before + incl - tsum;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid * kPer + j;
+      if (i < nblk) sCum[i] = run;
+      run += len[j];
+    }
+    if (tid == 0) sCum[nblk] = total;
+    __syncthreads();
+    const int G = (int)gridDim.x;
+    const int per = (int)(((long long)total + G - 1) / G + C::KT - 1) / C::KT * C::KT;
+    int pos = (int)min((long long)blockIdx.x * per, (long long)total);
+    const int end = (int)min((long long)pos + per, (long long)total);
+    // the block holding pos: the last i with sCum[i] <= pos (binary search)
+    int lo = 0, hi = nblk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sCum[mid] <= pos) lo = mid;
+      else hi = mid - 1;
+    }
+    for (int i = lo; pos < end && i < nblk; ++i) {
+      const int b0 = sCum[i], b1 = sCum[i + 1];
+      if (b1 <= pos) continue;  // an empty block
+      const int stop = min(end, b1);
+      __syncthreads();  // the previous piece's LDS reads are complete
+      process(i / n_tblocks, i % n_tblocks, pos - b0, stop - b0);
+      pos = stop;
+    }
   } else {
     // Persistent, per XCD: token blocks are numbered latest first
     // (descending work for causal-like windows) and block j belongs to XCD
@@ -449,7 +531,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       if (item >= n_items) break;
       __syncthreads();  // the previous item's LDS reads are complete
       const int rem = (item / n_chunks) * nx + x;  // block number, latest first
-      process(rem % B, n_tblocks - 1 - rem / B, item % n_chunks);
+      const int off = (item % n_chunks) * chunk_keys;
+      process(rem % B, n_tblocks - 1 - rem / B, off, off + chunk_keys);
     }
   }
 }
@@ -475,6 +558,14 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
   const long long items = tblocks * n_chunks;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (KP && tblocks <= kBalBlocks && tblocks * a.N <= 0x7fffffffLL) {
+    // key-parallel, balanced over the device-side windows (n_chunks = 0)
+    hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP, RT>), dim3((unsigned)slots),
+                       dim3(kIdxThreads), 0, stream, (const uint8_t*)a.q, a.q_scale,
+                       (const uint8_t*)a.k, a.k_scale, a.w, a.ks, a.ke, a.logits, (int)a.M,
+                       (int)a.N, (int)a.B, n_tblocks, 0, 0);
+    return hipGetLastError();
+  }
   const long long blocks = KP ? items : (items < slots ? items : slots);
   hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP, RT>), dim3((unsigned)blocks), dim3(kIdxThreads), 0,
                      stream, (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,

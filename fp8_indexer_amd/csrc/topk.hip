@@ -26,7 +26,9 @@
 // cuts them into 8192-key segments and reduces the segments' candidates, or,
 // when that launch's candidate buffer would be large, gives each row one
 // 512-thread workgroup that re-reads the row from L2 on each pass (digits
-// 12, 10, 10).  With few rows and N > 8192 every row is instead cut into
+// 12, 10, 10).  With few rows (decode) and 8192 < N <= 65536 one 1024-thread
+// workgroup per row holds the whole row in VGPRs (64 keys per lane), one
+// launch; with few rows and N > 65536 every row is instead cut into
 // 4096-key segments that share per-row digit histograms in global memory
 // (one launch per round).  Rows with len <= K only write s..e-1 and -1
 // padding.
@@ -349,12 +351,13 @@ constexpr int kRowThreads = kRowWaves * kWave;
 // One MSD round's threshold: hist[0..nb) counts the remaining keys by digit
 // (larger digit = larger key); returns the digit bin holding the krem-th
 // largest of them (x), the number of keys in the bins above it (y) and the
-// bin's own count (z).  Called by every thread of a kRowThreads workgroup;
-// hist may be in LDS or in global memory; sSel holds 3 ints.
+// bin's own count (z).  Called by every thread of a workgroup of W waves;
+// hist may be in LDS or in global memory; sRed holds W ints, sSel 3.
+template <int W = kRowWaves>
 __device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
                                               int* sSel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int bpt = nb / kRowThreads;  // bins per thread
+  const int bpt = nb / (W * kWave);  // bins per thread
   int tsum = 0;
   for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
   const int incl_w = wave_incl_scan(tsum);
@@ -362,7 +365,7 @@ __device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int 
   __syncthreads();
   int pre = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kRowWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     const int t = sRed[w];
     pre += w < wave ? t : 0;
     total += t;
@@ -394,11 +397,11 @@ __host__ __device__ constexpr int digit_shift(int round) {
 // whole row go to o in ascending position order.  gt0 / eq0: keys > tau /
 // == tau at positions before this workgroup's (other workgroups of the same
 // row).  Writes o[pos] = first + i, or cand[i] when GATHER.
-template <int KR, bool GATHER>
+template <int KR, bool GATHER, int W = kRowWaves>
 __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int len, uint32_t tau,
                                               int n_eq, int gt0, int eq0, int first,
                                               const int* __restrict__ cand, int K,
-                                              int* __restrict__ o, int (*sCnt)[kRowWaves]) {
+                                              int* __restrict__ o, int (*sCnt)[W]) {
   constexpr int SEG = kWave * KR;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int base = wave * SEG;
@@ -416,7 +419,7 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int le
   __syncthreads();
   int gt_base = gt0, eq_base = eq0;
 #pragma unroll
-  for (int w = 0; w < kRowWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     gt_base += w < wave ? sCnt[0][w] : 0;
     eq_base += w < wave ? sCnt[1][w] : 0;
   }
@@ -451,13 +454,13 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int le
 
 // Writes to o[0..K) the positions (first + i, or cand[i] when GATHER) of the
 // K largest of len > K keys src[i] (or src[cand[i]]), i < len, in ascending
-// order of i.  Keys at most 256*KR.  Workgroup of kRowThreads; the LDS
-// arrays are the caller's.
-template <int KR, bool GATHER>
+// order of i.  Keys at most 64*W*KR.  Workgroup of W waves; the LDS arrays
+// are the caller's.
+template <int KR, bool GATHER, int W = kRowWaves>
 __device__ __forceinline__ void row_select(const float* __restrict__ src,
                                            const int* __restrict__ cand, int len, int first,
                                            int K, int* __restrict__ o, uint32_t* hist, int* sRed,
-                                           int* sSel, int (*sCnt)[kRowWaves]) {
+                                           int* sSel, int (*sCnt)[W]) {
   constexpr int SEG = kWave * KR;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int base = wave * SEG;
@@ -483,9 +486,10 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
   // every key of that bin is selected, so the keys >= its smallest key (the
   // remaining digits zero) are exactly the K: the later rounds are skipped
   // (uniformly: the decision comes from LDS) and every key equal to that
-  // bound is taken.  Only with up to 16 keys per lane: with 32 the extra
-  // state costs registers, hence occupancy, which the long rows need more.
-  constexpr bool kEarly = KR <= 16;
+  // bound is taken.  Only with up to 16 keys per lane, or in the one-row-
+  // per-CU wide layout: with 32 in the 4-wave layout the extra state costs
+  // registers, hence occupancy, which the long rows need more.
+  constexpr bool kEarly = KR <= 16 || W > kRowWaves;
   uint32_t prefix = 0;
   int krem = K, above_total = 0, low_bits = 0;
 #pragma unroll
@@ -493,7 +497,7 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
     const int bits = digit_bits(round), shift = digit_shift(round);
     if (!kEarly || low_bits == 0) {
       const int nb = 1 << bits;
-      for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0u;
+      for (int i = tid; i < nb; i += W * kWave) hist[i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < KR; ++c) {
@@ -503,7 +507,7 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
           atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
-      const int3 sel = threshold_bin(hist, nb, krem, sRed, sSel);
+      const int3 sel = threshold_bin<W>(hist, nb, krem, sRed, sSel);
       prefix = (prefix << bits) | (uint32_t)sel.x;
       krem -= sel.y;
       above_total += sel.y;
@@ -512,7 +516,7 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
   }
   const uint32_t tau = kEarly ? prefix << low_bits : prefix;
   const int n_eq = kEarly && low_bits ? K : K - above_total;
-  emit_selected<KR, GATHER>(keys, len, tau, n_eq, 0, 0, first, cand, K, o, sCnt);
+  emit_selected<KR, GATHER, W>(keys, len, tau, n_eq, 0, 0, first, cand, K, o, sCnt);
 }
 
 #define DSA_TOPK_LDS                                  \
@@ -521,12 +525,18 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
   __shared__ int sSel[3];                             \
   __shared__ int sCnt[2][kRowWaves];
 
-template <int KR>
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
-                                                               const int* __restrict__ ks,
-                                                               const int* __restrict__ ke,
-                                                               int* __restrict__ out, int N, int K) {
-  DSA_TOPK_LDS
+// W waves per row (W = kRowWaves: many rows; W = 16: the wide layout for
+// few rows of up to 65536 keys, one 1024-thread workgroup per row and CU,
+// which replaces several launches over row segments with one).
+template <int KR, int W = kRowWaves>
+__global__ __launch_bounds__(W * kWave) void topk_row_kernel(const float* __restrict__ logits,
+                                                             const int* __restrict__ ks,
+                                                             const int* __restrict__ ke,
+                                                             int* __restrict__ out, int N, int K) {
+  __shared__ __align__(16) uint32_t hist[2048];
+  __shared__ int sRed[W];
+  __shared__ int sSel[3];
+  __shared__ int sCnt[2][W];
   const int tid = threadIdx.x;
   const size_t r = blockIdx.x;
   const int s = clampi(ks[r], 0, N);
@@ -534,12 +544,16 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   const int len = e - s;
   int* o = out + r * (size_t)K;
   if (len <= K) {
-    for (int i = tid; i < K; i += kRowThreads) o[i] = i < len ? s + i : -1;
+    for (int i = tid; i < K; i += W * kWave) o[i] = i < len ? s + i : -1;
     return;
   }
-  if (len > kRowThreads * KR) return;  // a long row: the long-row kernels take it
-  row_select<KR, false>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel, sCnt);
+  if (len > W * kWave * KR) return;  // a long row: the long-row kernels take it
+  row_select<KR, false, W>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel,
+                           sCnt);
 }
+
+constexpr int kWideWaves = 16, kWideKR = 64;
+constexpr int kWideKeys = kWideWaves * kWave * kWideKR;  // 65536
 
 // ---- long rows in two levels ----------------------------------------------
 // Level 1: the row is cut into segments of kSegKeys keys and each segment's
@@ -785,13 +799,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_split_emit_kernel(
 // Path of a call, chosen on the host from the sizes only (the windows are in
 // device memory): the bytes of scratch it needs.
 struct TopkPlan {
-  enum Path { kRows, kSplit, kTwoLevel } path;
+  enum Path { kRows, kWide, kSplit, kTwoLevel } path;
   int nseg;      // segments per row (split / two-level)
   size_t bytes;  // scratch
 };
 
 TopkPlan topk_plan(const TopkArgs& a) {
   const long long rows = a.B * a.M;
+  // Few rows (decode) of up to 65536 keys: one wide workgroup per row.
+  if (a.N > 8192 && a.N <= kWideKeys && rows < 256) return {TopkPlan::kWide, 1, 0};
   // Few rows (decode) with windows that may pass 8192 keys: several
   // workgroups per row, every row (see the split kernels).
   const long long split_nseg = (a.N + kSplitKeys - 1) / kSplitKeys;
@@ -830,6 +846,12 @@ hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream) {
   }
   TopkPlan plan = topk_plan(a);
   if (plan.bytes > 0 && (ws.ptr == nullptr || ws.bytes < plan.bytes)) plan.path = TopkPlan::kRows;
+  if (plan.path == TopkPlan::kWide) {
+    hipLaunchKernelGGL((topk_row_kernel<kWideKR, kWideWaves>), dim3((unsigned)rows),
+                       dim3(kWideWaves * kWave), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs,
+                       (int)a.N, (int)a.K);
+    return hipGetLastError();
+  }
   if (plan.path == TopkPlan::kSplit) {
     uint32_t* w = static_cast<uint32_t*>(ws.ptr);
     const int nseg = plan.nseg;

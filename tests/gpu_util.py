@@ -33,10 +33,12 @@ def indexer_gpu(x, N, logits_fill=float("nan")):
 
 def check_logits(gpu_rows, ref, terms, what=""):
     """gpu_rows, ref: [n, N] (ref NaN outside windows).  Inside: |d| <=
-    1e-4 * sum|terms|; outside: the GPU buffer must be untouched (NaN)."""
+    1e-4 * sum|terms| (an unwritten logit, still NaN, fails); outside: the
+    GPU buffer must be untouched (NaN)."""
     g = np.asarray(gpu_rows, np.float64)
     win = ~np.isnan(ref)
     assert np.all(np.isnan(g[~win])), f"{what}: logits written outside the window"
+    assert not np.isnan(g[win]).any(), f"{what}: {np.isnan(g[win]).sum()} window logits unwritten"
     d = np.abs(g[win] - ref[win])
     tol = 1e-4 * terms[win]
     bad = d > tol

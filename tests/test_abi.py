@@ -109,10 +109,12 @@ def test_topk_rejects_bad_arguments():
     assert call(A16, A16, A16, A16, 0, 4, 8, 2) == INVALID
     assert call(A16, A16, A16, A16, 1, 4, 8, 4097) == UNSUPPORTED
     assert call(A16, A16, ctypes.c_void_p(0x10001), A16, 1, 4, 8, 2) == INVALID
-    # decode-shaped rows need scratch: a workspace one byte short is refused
-    need = dsa.topk_workspace_size(64, 1, 65536, 2048)
-    assert call(A16, A16, A16, A16, 64, 1, 65536, 2048, ws=A16, wsb=need - 1) == WORKSPACE
-    assert call(A16, A16, A16, A16, 64, 1, 65536, 2048, ws=ctypes.c_void_p(0x10008),
+    # decode-shaped rows beyond 65536 keys need scratch: a workspace one byte
+    # short is refused
+    need = dsa.topk_workspace_size(64, 1, 131072, 2048)
+    assert need > 0
+    assert call(A16, A16, A16, A16, 64, 1, 131072, 2048, ws=A16, wsb=need - 1) == WORKSPACE
+    assert call(A16, A16, A16, A16, 64, 1, 131072, 2048, ws=ctypes.c_void_p(0x10008),
                 wsb=need) == INVALID  # workspace not 16-byte aligned
 
 
@@ -176,8 +178,10 @@ def test_workspace_size_queries():
     invalid shapes are rejected like the calls themselves."""
     assert dsa.topk_workspace_size(1, 4096, 4096, 2048) == 0
     assert dsa.topk_workspace_size(1, 4096, 8192, 2048) == 0
-    # 64 rows, N = 65536: 16 segments of 4096 keys per row
-    assert dsa.topk_workspace_size(64, 1, 65536, 2048) == 64 * (6144 + 16 * 1028) * 4
+    # few rows of up to 65536 keys: one workgroup per row, no scratch
+    assert dsa.topk_workspace_size(64, 1, 65536, 2048) == 0
+    # 64 rows, N = 131072: 32 segments of 4096 keys per row
+    assert dsa.topk_workspace_size(64, 1, 131072, 2048) == 64 * (6144 + 32 * 1028) * 4
     # 300 rows of 20000 keys: 3 segments of 8192 keys, K candidates each
     assert dsa.topk_workspace_size(1, 300, 20000, 100) == 300 * 3 * 100 * 4
     # candidates beyond 256 MiB: none (streaming)

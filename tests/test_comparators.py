@@ -67,6 +67,9 @@ def test_check_logits_catches_value_and_window_mistakes():
     g = gpu.copy()
     g[0, 5] = 0.0                            # row 0's window is [0, 1): written outside it
     _expect_fail(check_logits, g, ref, terms)
+    g = gpu.copy()
+    g[r, c] = np.nan                         # a window logit left unwritten
+    _expect_fail(check_logits, g, ref, terms)
 
 
 def test_check_attn_catches_output_mistakes():

@@ -71,6 +71,25 @@ def test_attn_small(Hq, Dqk, Dv, K, fp8, sink, kind):
     check_attn(o, ref, f"Hq{Hq}/{Dqk}/{K}/{kind}")
 
 
+@pytest.mark.parametrize("sink", [True, False])
+@pytest.mark.parametrize("kind", ["full", "ragged", "messy"])
+@pytest.mark.parametrize("K", [1, 31, 32, 33, 77, 300, 2048, 3000])
+def test_attn_unsplit_128_heads(K, kind, sink):
+    """128 heads, bf16, no workspace: the unsplit instance (two waves per
+    SIMD for K <= 2048; K = 3000 takes the one-wave-per-SIMD kernel), at
+    tile-boundary lengths, with empty, ragged and messy index lists."""
+    B, M, N = 2, 3, 3000
+    wl = W.Workload("u", B=B, M=M, N=N, H=4, D=64, K=K, Hq=128, Dqk=576, Dv=512, seed=K + 5)
+    log(f"attn unsplit 128 heads K={K} {kind} sink={sink}")
+    x = W.make_inputs(wl, parts=("attn",))
+    if not sink:
+        x["sink"] = None
+    idx = _indices(np.random.default_rng(K + 1), B, M, N, K, kind)
+    o = _run(x, idx, wl, workspace=None)
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv)
+    check_attn(o, ref, f"unsplit K{K}/{kind}")
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_attn_all_invalid_rows_are_zero(fp8):
     B, M, N, K = 1, 4, 500, 64

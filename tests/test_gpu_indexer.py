@@ -78,6 +78,28 @@ def test_indexer_decode_layouts(H, D, M):
     check_logits(g, ref, terms, f"decode H{H}D{D}M{M}")
 
 
+@pytest.mark.parametrize("B,N,empty", [(300, 3000, 0.5), (1100, 300, 0.2)])
+def test_indexer_decode_balance(B, N, empty):
+    """One token per batch entry.  Up to 1024 entries: the windows laid end
+    to end are cut into equal ranges, one per workgroup, which straddle
+    entries (about half of them empty here, lengths 1 to N).  Beyond 1024
+    entries: one item per (entry, key chunk)."""
+    wl = _small(64, 128, M=1, N=N, B=B, seed=B)
+    log(f"indexer decode balance B={B} N={N}")
+    x = W.make_inputs(wl, parts=("indexer",))
+    rng = np.random.default_rng(B)
+    ks = rng.integers(0, N, (B, 1)).astype(np.int32)
+    ke = (ks + rng.integers(1, N + 1, (B, 1))).astype(np.int32)  # past the end: clamped
+    ke[rng.random((B, 1)) < empty] = 0                            # empty
+    ks[0, 0], ke[0, 0] = 0, N
+    ks[B - 1, 0], ke[B - 1, 0] = N - 1, N                           # one key
+    x["ks"], x["ke"] = ks, ke
+    g = indexer_gpu(x, wl.N).cpu().numpy().reshape(-1, wl.N)
+    ref, terms = oracle.indexer_logits(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"],
+                                       ks, ke, with_terms=True)
+    check_logits(g, ref, terms, f"decode balance B{B}")
+
+
 WORKLOAD_ROWS = {"tiny_causal_256": None, "prefill_4096": 40, "varlen_4x8192": 24,
                  "decode_b64": 12, "prefill_8192_fp8kv": 24}
 

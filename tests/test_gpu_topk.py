@@ -69,9 +69,10 @@ def test_topk_small(kind, K):
 
 @pytest.mark.parametrize("workspace", ["auto", None], ids=["split", "streaming"])
 def test_topk_long_rows(workspace):
-    """Rows longer than the register-resident limit (8192 keys), few rows:
-    with a workspace the rows are split into segments sharing digit
-    histograms; without one each long row takes one streaming workgroup."""
+    """Rows longer than the register-resident limit (8192 keys), few rows,
+    N > 65536: with a workspace the rows are split into segments sharing
+    digit histograms; without one each long row takes one streaming
+    workgroup."""
     rng = np.random.default_rng(11)
     B, M, N, K = 2, 3, 70000, 2048
     lg = _dist("special", (B, M, N), rng)
@@ -113,20 +114,25 @@ def test_topk_workloads(name, nrows):
     _compare(lg_t, ks, ke, wl.K, rows=rows, what=name + "/ties")
 
 
+@pytest.mark.parametrize("N", [40000, 65536, 70000], ids=["wide", "wide_max", "split"])
 @pytest.mark.parametrize("kind", ["special", "ties", "narrow"])
 @pytest.mark.parametrize("K", [100, 2048, 4096])
-def test_topk_split_rows(kind, K):
-    """Few rows with N > 8192: every row is cut into 4096-key segments, one
-    workgroup each, that share the row's digit histograms; lengths straddle
-    segment boundaries."""
-    rng = np.random.default_rng(K + len(kind))
-    B, M, N = 1, 10, 40000
+def test_topk_few_long_rows(kind, K, N):
+    """Few rows with N > 8192.  N <= 65536: one 1024-thread workgroup per
+    row with the row in registers (lengths straddle the 4096-key wave
+    segments).  N > 65536: every row is cut into 4096-key segments, one
+    workgroup each, that share the row's digit histograms (lengths straddle
+    segment boundaries)."""
+    rng = np.random.default_rng(K + len(kind) + N)
+    B, M = 1, 10
     lg = _dist(kind, (B, M, N), rng)
     # ... plus an empty row and a row shorter than K (written as -1 padded)
     ks = np.array([[0, 0, 0, 0, 0, 100, 31000, 5, 7, 0]], np.int32)
     ke = np.array([[N, K + 1, 8192, 8193, 16384 + 7, 24000, N, 5 + K, 7, K - 1]], np.int32)
-    log(f"topk split rows {kind} K={K}")
-    _compare(lg, ks, ke, K, what=f"split rows {kind}/K{K}")
+    wide = N <= 65536
+    assert (dsa.topk_workspace_size(B, M, N, K) == 0) == wide
+    log(f"topk few long rows {kind} K={K} N={N}")
+    _compare(lg, ks, ke, K, what=f"few long rows {kind}/K{K}/N{N}")
 
 
 @pytest.mark.parametrize("workspace", ["auto", None], ids=["two_level", "streaming"])
