@@ -67,8 +67,9 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kBI = 64;                  // gathered rows per tile
 constexpr int kUnits = kDqk / 16;        // 16-byte units per row
-constexpr int kUS = kBI * 16 + 64;       // LDS stride of a unit (bytes): 64 rows + 64 pad
-constexpr int kTile = kUnits * kUS;      // LDS tile (bytes)
+constexpr int kBlocks = kUnits;          // LDS blocks per tile: 9 64-byte chunks x 4 row groups
+constexpr int kBS = 16 * 64 + 64;        // LDS stride of a block (bytes): 16 rows x 64 + 64 pad
+constexpr int kTile = kBlocks * kBS;     // LDS tile (bytes)
 constexpr int kKS = kDqk / 64;           // 64-deep k-steps of QK^T
 constexpr int kThreads = 256;
 constexpr int kMaxK = 4096;
@@ -101,13 +102,16 @@ __device__ __forceinline__ void qk_drain(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
-// LDS tile layout, unit-major: the 16-byte unit u of tile row r is at
-// u * kUS + 16 r.  A 64-lane direct load then fills one unit of all 64 rows
-// (lane l: row l), so a lane's global address is its row's address plus
-// 16 u.  The QK^T operand read (32 consecutive rows of one unit) is
-// conflict-free, and the 64-byte pad after each unit puts the two 16-column
-// halves of a transposing read (units u and u+1, 8 rows x 16 bytes each)
-// on different banks.
+// LDS tile layout: block (c, G) holds bytes [64c, 64c+64) (chunk c) of tile
+// rows [16G, 16G+16) at (4c + G) * kBS; inside it, the 16-byte unit p of
+// row r (0..15) sits at slot 4r + (p ^ sw(r)), sw(r) = (r >> 2) & 3.  One
+// 64-lane direct load fills one block, 4 lanes per row: 16 rows x 64
+// contiguous bytes, i.e. 16 cache lines (one 16-byte unit of 64 rows per
+// load touched 64, and the memory pipeline takes a gather load at about
+// one line per cycle).  The swizzle keeps the QK^T operand read (16 rows,
+// one unit each, per 16 lanes) and the transposing V read (8 rows x 16
+// bytes per 16 lanes, 32 lanes per pass) free of bank conflicts.
+__device__ __forceinline__ int unit_slot(int r, int p) { return 4 * r + (p ^ ((r >> 2) & 3)); }
 
 // Workgroup barriers without the release fence of __syncthreads(), which
 // waits for every outstanding global load, the direct-to-LDS loads of a
@@ -294,18 +298,19 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   // LDS address of tile buffer 0 (the others follow at kTile-byte steps)
   const uint32_t kv_lds =
       (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(&sKV[0][0]);
-  // this lane's row of a tile, at this wave's first unit (invalid slots:
-  // the tile's first valid row)
+  // Wave w fills row group w (rows 16w..16w+15), chunks 0..8: lane l
+  // writes slot l of the block, i.e. unit (l & 3) ^ sw(l >> 2) of row
+  // 16w + (l >> 2) (invalid slots: the tile's first valid row).
   auto row_src = [&](int tile) __attribute__((always_inline)) {
-    const int v = sIdx[tile * kBI + lane];
-    return kvb + (size_t)(v ^ (v >> 31)) * kDqk + 16 * wave;
+    const int v = sIdx[tile * kBI + 16 * wave + (lane >> 2)];
+    return kvb + (size_t)(v ^ (v >> 31)) * kDqk + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
   };
-  // unit wave + 4k of the tile whose row addresses are in src
+  // chunk k of this wave's row group, for the tile whose row addresses are in src
   auto issue_unit = [&](const uint8_t* src, int k, int buf) __attribute__((always_inline)) {
-    const uint32_t lds = kv_lds + buf * kTile + wave * kUS;
+    const uint32_t lds = kv_lds + buf * kTile + wave * kBS;
     switch (k) {  // the global offset 64 k is an immediate (added to the LDS address too)
 #define DSA_F8_UNIT(K) \
-  case K: lds_dma16<64 * K>(src, __builtin_amdgcn_readfirstlane(lds + K * (4 * kUS - 64))); break;
+  case K: lds_dma16<64 * K>(src, __builtin_amdgcn_readfirstlane(lds + K * (4 * kBS - 64))); break;
       DSA_F8_UNIT(0) DSA_F8_UNIT(1) DSA_F8_UNIT(2) DSA_F8_UNIT(3) DSA_F8_UNIT(4)
       DSA_F8_UNIT(5) DSA_F8_UNIT(6) DSA_F8_UNIT(7) DSA_F8_UNIT(8)
 #undef DSA_F8_UNIT
@@ -341,13 +346,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   float xmax = -INFINITY;  // largest x - m seen (first pass: overflow check)
   f32x16 sacc[NT];         // S^T of the tile in flight
 
-  // QK^T operand: lane (r, g) of row half tau reads row 32 tau + r, logical
-  // units 4s + 2g and 4s + 2g + 1 of k-step s
-  const int aoff0 = (2 * g) * kUS + 16 * (32 * tau0 + hl);
-  const int aoff1 = aoff0 + kUS;
+  // QK^T operand: lane (r, g) of row half tau reads row 32 tau + r, units
+  // 2g and 2g + 1 of chunk s (k-step s): row group 2 tau + r / 16
+  const int aoff0 = (2 * tau0 + (hl >> 4)) * kBS + 16 * unit_slot(hl & 15, 2 * g);
+  const int aoff1 = (2 * tau0 + (hl >> 4)) * kBS + 16 * unit_slot(hl & 15, 2 * g + 1);
   auto lda = [&](const uint8_t* sK, int s, int u) __attribute__((always_inline)) {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(sK + aoff0 + 512 * u + 4 * kUS * s);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(sK + aoff1 + 512 * u + 4 * kUS * s);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(sK + aoff0 + (4 * s + 2 * u) * kBS);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(sK + aoff1 + (4 * s + 2 * u) * kBS);
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   // QK^T of a tile, one k-step at a time (the next step's operands are read
@@ -400,21 +405,23 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   };
 
   // V^T A-fragment of output column tile t: slot 8q + r of lane half g is
-  // row 32(q>>1) + 8(2(q&1) + (r>>2)) + 4g + (r&3), r = the row the lane
-  // pair (2r, 2r+1) of each 16-lane group addresses; the lane's 8 bytes are
-  // logical unit c0/16 + 2t + ch, half l16 & 1.
+  // row 16q + rr, rr = 8(r>>2) + 4g + (r&3), r = the row the lane pair (2r,
+  // 2r+1) of each 16-lane group addresses; the lane's 8 bytes are half
+  // l16 & 1 of unit c0/16 + 2t + ch: chunk c0/64 + t/2, unit 2(t&1) + ch,
+  // row group q.
   const int l16 = lane & 15, trr = l16 >> 1, ch = (lane >> 4) & 1;
-  int voff;  // row rr of read 0 at unit c0/16 + ch; reads q add 16 rows, tile t 2 units
+  int vo[2];  // read 0 of an even / odd column tile, within chunk c0/64
   {
     const int rr = 8 * (trr >> 2) + 4 * g + (trr & 3);
-    voff = (c0 / 16 + ch) * kUS + 16 * rr + 8 * (l16 & 1);
+    vo[0] = (c0 / 64) * 4 * kBS + 16 * unit_slot(rr, ch) + 8 * (l16 & 1);
+    vo[1] = (c0 / 64) * 4 * kBS + 16 * unit_slot(rr, 2 + ch) + 8 * (l16 & 1);
   }
   auto vfrag = [&](const uint8_t* sK, int t) __attribute__((always_inline)) {
-    const uint8_t* vp = sK + voff + 2 * kUS * t;
+    const uint8_t* vp = sK + vo[t & 1] + 4 * kBS * (t >> 1);
     const i32x2 r0 = lds_read_tr8(vp);
-    const i32x2 r1 = lds_read_tr8(vp + 16 * 16);
-    const i32x2 r2 = lds_read_tr8(vp + 16 * 32);
-    const i32x2 r3 = lds_read_tr8(vp + 16 * 48);
+    const i32x2 r1 = lds_read_tr8(vp + kBS);
+    const i32x2 r2 = lds_read_tr8(vp + 2 * kBS);
+    const i32x2 r3 = lds_read_tr8(vp + 3 * kBS);
     return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   };
 
