@@ -7,12 +7,13 @@
 // valid.  The value is the first Dv columns of the same latent row.
 //
 // Design (MI355X-first):
-//  * One workgroup per query token.  With 128 heads it has 8 waves (two per
-//    SIMD) of 16 heads each; fewer heads use fewer waves.  A wave's q rows
-//    are MFMA B-fragments held in registers for the whole token, except for
-//    the last few 32-deep k-steps, which sit in LDS: 16 heads x 512 fp32 O
-//    accumulators and the q fragments would otherwise fill the 256 VGPRs a
-//    wave gets at two waves per SIMD.
+//  * One workgroup per query token.  With 128 heads it has 4 waves (one per
+//    SIMD) of 32 heads each; fewer heads use 16 per wave and fewer waves.  A
+//    wave's q rows are MFMA B-fragments held in registers for the whole
+//    token, except for the last few 32-deep k-steps, which sit in LDS: the
+//    O accumulators (128 heads x 128 columns, fp32) fill the 256 AGPRs and
+//    q, the score accumulators and the staged KV chunks share the 256
+//    VGPRs.
 //  * The product is formed transposed, S^T[j, h] = kv_j . q_h, on
 //    v_mfma_f32_16x16x32_bf16.  In the C layout each lane then holds one head
 //    and 8 gathered rows, which is the B-fragment layout of the next product
