@@ -357,7 +357,8 @@ template <int W = kRowWaves>
 __device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int krem, int* sRed,
                                               int* sSel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int bpt = nb / (W * kWave);  // bins per thread
+  // bins per thread; with fewer bins than threads, thread t owns bin t
+  const int bpt = nb >= W * kWave ? nb / (W * kWave) : (tid < nb ? 1 : 0);
   int tsum = 0;
   for (int j = 0; j < bpt; ++j) tsum += (int)hist[tid * bpt + j];
   const int incl_w = wave_incl_scan(tsum);
@@ -386,8 +387,72 @@ __device__ __forceinline__ int3 threshold_bin(const uint32_t* hist, int nb, int 
   return make_int3(sSel[0], sSel[1], sSel[2]);
 }
 
+// The same for a compile-time bin count NB, as the register-resident row
+// kernels use it: each thread reads its NB / (64 W) consecutive bins once
+// (16-byte reads when they come in fours, which keeps the 64 lanes of a read
+// on distinct banks) and scans them from registers; with fewer bins than
+// threads, thread t holds bin t.
+template <int W, int NB>
+__device__ __forceinline__ int3 threshold_bin_n(const uint32_t* hist, int krem, int* sRed,
+                                                int* sSel) {
+  constexpr int T = W * kWave, BPT = NB >= T ? NB / T : 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  uint32_t h[BPT];
+  if constexpr (BPT % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < BPT / 4; ++q) {
+      const uint4 x = reinterpret_cast<const uint4*>(hist + tid * BPT)[q];
+      h[4 * q] = x.x;
+      h[4 * q + 1] = x.y;
+      h[4 * q + 2] = x.z;
+      h[4 * q + 3] = x.w;
+    }
+  } else if constexpr (NB >= T) {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) h[j] = hist[tid * BPT + j];
+  } else {
+    h[0] = tid < NB ? hist[tid] : 0u;
+  }
+  int tsum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) tsum += (int)h[j];
+  const int incl_w = wave_incl_scan(tsum);
+  if (lane == 63) sRed[wave] = incl_w;
+  __syncthreads();
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int t = sRed[w];
+    pre += w < wave ? t : 0;
+    total += t;
+  }
+  int above = total - (pre + incl_w);  // keys in bins of higher threads
+  if (above < krem && krem <= above + tsum) {  // exactly one thread
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      const int c = (int)h[j];
+      if (above < krem && krem <= above + c) {
+        sSel[0] = tid * BPT + j;
+        sSel[1] = above;
+        sSel[2] = c;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+  return make_int3(sSel[0], sSel[1], sSel[2]);
+}
+
 // Digit layout of the 32-bit key: rounds of 11, 11 and 10 bits.
 __host__ __device__ constexpr int digit_bits(int round) { return round < 2 ? 11 : 10; }
+// Register-resident rows: a first digit of B0 bits, then the remaining
+// 32 - B0 bits in two rounds (B0 = 11: 11, 11, 10; B0 = 13: 13, 10, 9).
+__host__ __device__ constexpr int rdigit_bits(int b0, int round) {
+  return round == 0 ? b0 : (round == 1 ? (33 - b0) / 2 : 32 - b0 - (33 - b0) / 2);
+}
+__host__ __device__ constexpr int rdigit_shift(int b0, int round) {
+  return round == 0 ? 32 - b0 : (round == 1 ? 32 - b0 - rdigit_bits(b0, 1) : 0);
+}
 __host__ __device__ constexpr int digit_shift(int round) {
   return round == 0 ? 21 : (round == 1 ? 10 : 0);
 }
@@ -452,11 +517,59 @@ __device__ __forceinline__ void emit_selected(const uint32_t (&keys)[KR], int le
   }
 }
 
+// Keys of the register-resident rows are tested against the row length only
+// once per kChunk slots: the keys of positions >= len are 0, which no key of
+// a real value reaches (order_key maps -inf and NaN to 0x007FFFFF), so the
+// few that a chunk holds land in bin 0 of the first round, which never holds
+// the threshold (len > K real keys lie above it), and are never selected.
+constexpr int kChunk = 8;
+
+// Emission when exactly the keys >= tau are selected (K of them, no tie to
+// rank): a wave's selected keys go to consecutive slots after those of the
+// waves before it, in position order.  Layout and GATHER as emit_selected.
+template <int KR, bool GATHER, int W = kRowWaves>
+__device__ __forceinline__ void emit_at_least(const uint32_t (&keys)[KR], int len, uint32_t tau,
+                                              int first, const int* __restrict__ cand, int K,
+                                              int* __restrict__ o, int (*sCnt)[W]) {
+  constexpr int SEG = kWave * KR;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int base = wave * SEG;
+  int cnt = 0;  // per lane, summed over the wave below
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    if (c % kChunk == 0 && base + c * kWave >= len) break;
+    cnt += keys[c] >= tau ? 1 : 0;
+  }
+  cnt = wave_incl_scan(cnt);
+  if (lane == 63) sCnt[0][wave] = cnt;
+  __syncthreads();
+  int run = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) run += w < wave ? sCnt[0][w] : 0;
+  // stores through a buffer resource of K entries (its range check drops
+  // any slot past o[K - 1])
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(o, (short)0, K * 4, 0x00020000);
+#pragma unroll
+  for (int c = 0; c < KR; ++c) {
+    if (c % kChunk == 0 && base + c * kWave >= len) break;
+    const int i = base + c * kWave + lane;
+    const bool sel = keys[c] >= tau;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
+    if (sel) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)run));
+      __builtin_amdgcn_raw_buffer_store_b32(GATHER ? cand[i] : first + i, ro, pos * 4, 0, 0);
+    }
+    run += (int)__popcll(m);
+  }
+}
+
 // Writes to o[0..K) the positions (first + i, or cand[i] when GATHER) of the
 // K largest of len > K keys src[i] (or src[cand[i]]), i < len, in ascending
 // order of i.  Keys at most 64*W*KR.  Workgroup of W waves; the LDS arrays
 // are the caller's.
-template <int KR, bool GATHER, int W = kRowWaves>
+template <int KR, bool GATHER, int W = kRowWaves, int B0 = 11>
 __device__ __forceinline__ void row_select(const float* __restrict__ src,
                                            const int* __restrict__ cand, int len, int first,
                                            int K, int* __restrict__ o, uint32_t* hist, int* sRed,
@@ -491,32 +604,46 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
   // registers, hence occupancy, which the long rows need more.
   constexpr bool kEarly = KR <= 16 || W > kRowWaves;
   uint32_t prefix = 0;
-  int krem = K, above_total = 0, low_bits = 0;
+  int krem = K, above_total = 0, low_bits = 0, last_z = 0;
 #pragma unroll
   for (int round = 0; round < 3; ++round) {
-    const int bits = digit_bits(round), shift = digit_shift(round);
+    const int bits = rdigit_bits(B0, round), shift = rdigit_shift(B0, round);
     if (!kEarly || low_bits == 0) {
       const int nb = 1 << bits;
       for (int i = tid; i < nb; i += W * kWave) hist[i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < KR; ++c) {
-        if (base + c * kWave >= len) break;  // wave-uniform: rest of the segment is empty
+        // wave-uniform: the rest of the segment is empty
+        if (c % kChunk == 0 && base + c * kWave >= len) break;
         const uint32_t u = keys[c];
         if (round == 0 || (u >> (shift + bits)) == prefix)
           atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
-      const int3 sel = threshold_bin<W>(hist, nb, krem, sRed, sSel);
+      int3 sel;
+      if (round == 0)
+        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 0)>(hist, krem, sRed, sSel);
+      else if (round == 1)
+        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 1)>(hist, krem, sRed, sSel);
+      else
+        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 2)>(hist, krem, sRed, sSel);
       prefix = (prefix << bits) | (uint32_t)sel.x;
       krem -= sel.y;
       above_total += sel.y;
+      last_z = sel.z;
       if (kEarly && sel.z == krem) low_bits = shift;
     }
   }
   const uint32_t tau = kEarly ? prefix << low_bits : prefix;
-  const int n_eq = kEarly && low_bits ? K : K - above_total;
-  emit_selected<KR, GATHER, W>(keys, len, tau, n_eq, 0, 0, first, cand, K, o, sCnt);
+  // all keys >= tau are selected after an early stop, or when the keys equal
+  // to the full 32-bit tau are exactly the ones still needed
+  if ((kEarly && low_bits) || last_z == krem) {
+    emit_at_least<KR, GATHER, W>(keys, len, tau, first, cand, K, o, sCnt);
+  } else {
+    const int n_eq = K - above_total;
+    emit_selected<KR, GATHER, W>(keys, len, tau, n_eq, 0, 0, first, cand, K, o, sCnt);
+  }
 }
 
 #define DSA_TOPK_LDS                                  \
@@ -528,12 +655,12 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 // W waves per row (W = kRowWaves: many rows; W = 16: the wide layout for
 // few rows of up to 65536 keys, one 1024-thread workgroup per row and CU,
 // which replaces several launches over row segments with one).
-template <int KR, int W = kRowWaves>
+template <int KR, int W = kRowWaves, int B0 = 11>
 __global__ __launch_bounds__(W * kWave) void topk_row_kernel(const float* __restrict__ logits,
                                                              const int* __restrict__ ks,
                                                              const int* __restrict__ ke,
                                                              int* __restrict__ out, int N, int K) {
-  __shared__ __align__(16) uint32_t hist[2048];
+  __shared__ __align__(16) uint32_t hist[1 << (B0 > 11 ? B0 : 11)];
   __shared__ int sRed[W];
   __shared__ int sSel[3];
   __shared__ int sCnt[2][W];
@@ -548,11 +675,18 @@ __global__ __launch_bounds__(W * kWave) void topk_row_kernel(const float* __rest
     return;
   }
   if (len > W * kWave * KR) return;  // a long row: the long-row kernels take it
-  row_select<KR, false, W>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel,
-                           sCnt);
+  row_select<KR, false, W, B0>(logits + r * (size_t)N + s, nullptr, len, s, K, o, hist, sRed, sSel,
+                               sCnt);
 }
 
 constexpr int kWideWaves = 16, kWideKR = 64;
+// First-digit width of the register-resident row kernels (tuning knobs)
+#ifndef DSA_TOPK_B0_ROW
+#define DSA_TOPK_B0_ROW 11
+#endif
+#ifndef DSA_TOPK_B0_WIDE
+#define DSA_TOPK_B0_WIDE 13
+#endif
 constexpr int kWideKeys = kWideWaves * kWave * kWideKR;  // 65536
 
 // ---- long rows in two levels ----------------------------------------------
@@ -839,7 +973,7 @@ hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream) {
   constexpr int kShort = kRowThreads * (8192 / kRowThreads);  // register-resident rows
   // Rows of up to 4096 keys: kRowWaves waves per row, keys in VGPRs.
   if (a.N <= kRowThreads * (4096 / kRowThreads)) {
-    hipLaunchKernelGGL(topk_row_kernel<4096 / kRowThreads>, dim3((unsigned)rows),
+    hipLaunchKernelGGL((topk_row_kernel<4096 / kRowThreads, kRowWaves, DSA_TOPK_B0_ROW>), dim3((unsigned)rows),
                        dim3(kRowThreads), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N,
                        (int)a.K);
     return hipGetLastError();
@@ -847,7 +981,7 @@ hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream) {
   TopkPlan plan = topk_plan(a);
   if (plan.bytes > 0 && (ws.ptr == nullptr || ws.bytes < plan.bytes)) plan.path = TopkPlan::kRows;
   if (plan.path == TopkPlan::kWide) {
-    hipLaunchKernelGGL((topk_row_kernel<kWideKR, kWideWaves>), dim3((unsigned)rows),
+    hipLaunchKernelGGL((topk_row_kernel<kWideKR, kWideWaves, DSA_TOPK_B0_WIDE>), dim3((unsigned)rows),
                        dim3(kWideWaves * kWave), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs,
                        (int)a.N, (int)a.K);
     return hipGetLastError();
@@ -874,7 +1008,7 @@ hipError_t launch_topk(const TopkArgs& a, Workspace ws, hipStream_t stream) {
   const int skip_len = rows_first ? kShort : 0;
   hipError_t err = hipSuccess;
   if (rows_first) {
-    hipLaunchKernelGGL(topk_row_kernel<8192 / kRowThreads>, dim3((unsigned)rows),
+    hipLaunchKernelGGL((topk_row_kernel<8192 / kRowThreads, kRowWaves, DSA_TOPK_B0_ROW>), dim3((unsigned)rows),
                        dim3(kRowThreads), 0, stream, a.logits, a.ks, a.ke, a.topk_idxs, (int)a.N,
                        (int)a.K);
     err = hipGetLastError();
