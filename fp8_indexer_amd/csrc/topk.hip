@@ -4,8 +4,9 @@
 // order-preserving unsigned keys; a histogram of the leading key bits and a
 // cumulative sum locate the bin that holds the K-th largest value; only that
 // bin is refined on the next bits, so the exact threshold is found without
-// sorting the row.  Here the 32-bit key is resolved in three MSD rounds
-// (11, 11, 10 bits, or 12, 10, 10 for rows beyond 8192 keys) with LDS
+// sorting the row.  Here the 32-bit key is resolved in up to three MSD
+// rounds (11, 11, 10 bits; 12, 10, 10 for rows streamed from L2; 13, 10, 9
+// for rows of up to 65536 keys held by one 1024-thread workgroup) with LDS
 // histograms.
 //
 // Selection rule (this library's contract): the K keys of [s, e) first in
@@ -19,8 +20,8 @@
 //
 // Rows whose window has up to 8192 keys: one 256-thread workgroup per row,
 // each wave holding a contiguous quarter of the row in VGPRs (digits of 11,
-// 11 and 10 bits, a shared LDS histogram, wave-level scans; with up to 4096
-// keys the rounds stop early once the threshold bin is wholly selected).
+// 11 and 10 bits, a shared LDS histogram, wave-level scans; the rounds stop
+// early once the threshold bin is wholly selected).
 // The path is chosen per row from its own window, not from N: longer
 // windows (only possible when N > 8192) are left to a second launch, which
 // cuts them into 8192-key segments and reduces the segments' candidates, or,
@@ -45,8 +46,10 @@ constexpr int kEPT = 16;  // register-resident keys per lane
 // Order-preserving key: larger float -> larger unsigned key.  NaN -> key of
 // -inf; -0 -> key of +0.
 __device__ __forceinline__ uint32_t order_key(float v) {
-  const float z = v + 0.0f;  // -0 -> +0 (IEEE sum of opposite zeros); NaN stays NaN
-  const uint32_t b = __builtin_isnan(z) ? 0xFF800000u : __float_as_uint(z);  // NaN -> -inf
+  // -0 -> +0 (IEEE sum of opposite zeros); NaN -> -inf (maxNum returns the
+  // operand that is not NaN)
+  const float z = __builtin_fmaxf(v + 0.0f, -__builtin_inff());
+  const uint32_t b = __float_as_uint(z);
   // negative: all bits flipped; positive: sign bit set
   return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
@@ -546,6 +549,7 @@ __device__ __forceinline__ void emit_at_least(const uint32_t (&keys)[KR], int le
   int run = 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) run += w < wave ? sCnt[0][w] : 0;
+  run = __builtin_amdgcn_readfirstlane(run);  // wave-uniform: keep it scalar
   // stores through a buffer resource of K entries (its range check drops
   // any slot past o[K - 1])
   const __amdgpu_buffer_rsrc_t ro =
@@ -557,9 +561,10 @@ __device__ __forceinline__ void emit_at_least(const uint32_t (&keys)[KR], int le
     const bool sel = keys[c] >= tau;
     const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
     if (sel) {
-      const int pos = (int)__builtin_amdgcn_mbcnt_hi(
-          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)run));
-      __builtin_amdgcn_raw_buffer_store_b32(GATHER ? cand[i] : first + i, ro, pos * 4, 0, 0);
+      // slot run + (selected lanes below): the wave's part goes in soffset
+      const int below = lanes_below(m);
+      __builtin_amdgcn_raw_buffer_store_b32(GATHER ? cand[i] : first + i, ro, below * 4, run * 4,
+                                            0);
     }
     run += (int)__popcll(m);
   }
@@ -593,22 +598,23 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 #pragma unroll
     for (int c = 0; c < KR; ++c) keys[c] = order_key(v[c]);
   }
-  mask_tail<KR>(keys, base + lane, len);
+  // only the wave that holds the row's end has slots past it (later waves
+  // skip all their slots)
+  if (base < len && len < base + SEG) mask_tail<KR>(keys, base + lane, len);
 
   // After a round whose threshold bin holds exactly the keys still needed,
   // every key of that bin is selected, so the keys >= its smallest key (the
   // remaining digits zero) are exactly the K: the later rounds are skipped
   // (uniformly: the decision comes from LDS) and every key equal to that
-  // bound is taken.  Only with up to 16 keys per lane, or in the one-row-
-  // per-CU wide layout: with 32 in the 4-wave layout the extra state costs
-  // registers, hence occupancy, which the long rows need more.
-  constexpr bool kEarly = KR <= 16 || W > kRowWaves;
+  // bound is taken.
   uint32_t prefix = 0;
   int krem = K, above_total = 0, low_bits = 0, last_z = 0;
+  uint32_t one = 1u;  // the atomics' operand, kept in one register
+  asm volatile("" : "+v"(one));
 #pragma unroll
   for (int round = 0; round < 3; ++round) {
     const int bits = rdigit_bits(B0, round), shift = rdigit_shift(B0, round);
-    if (!kEarly || low_bits == 0) {
+    if (low_bits == 0) {
       const int nb = 1 << bits;
       for (int i = tid; i < nb; i += W * kWave) hist[i] = 0u;
       __syncthreads();
@@ -617,8 +623,20 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
         // wave-uniform: the rest of the segment is empty
         if (c % kChunk == 0 && base + c * kWave >= len) break;
         const uint32_t u = keys[c];
-        if (round == 0 || (u >> (shift + bits)) == prefix)
-          atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+        if (round == 0) {
+          atomicAdd(&hist[u >> shift], one);
+        } else if (shift != 0) {
+          // the keys under the prefix are those whose digit offset
+          // (u >> shift) - (prefix << bits) is below nb; as a byte offset,
+          // which cannot wrap into [0, 4 nb) while u >> shift < 2^29
+          const uint32_t a = (__builtin_amdgcn_ubfe(u, shift, 32 - shift) << 2) -
+                             (prefix << (bits + 2));
+          if (a < (uint32_t)(4 * nb))
+            atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + a), one);
+        } else {
+          const uint32_t d = u - (prefix << bits);
+          if (d < (uint32_t)nb) atomicAdd(&hist[d], one);
+        }
       }
       __syncthreads();
       int3 sel;
@@ -632,13 +650,13 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
       krem -= sel.y;
       above_total += sel.y;
       last_z = sel.z;
-      if (kEarly && sel.z == krem) low_bits = shift;
+      if (sel.z == krem) low_bits = shift;
     }
   }
-  const uint32_t tau = kEarly ? prefix << low_bits : prefix;
+  const uint32_t tau = prefix << low_bits;
   // all keys >= tau are selected after an early stop, or when the keys equal
   // to the full 32-bit tau are exactly the ones still needed
-  if ((kEarly && low_bits) || last_z == krem) {
+  if (low_bits || last_z == krem) {
     emit_at_least<KR, GATHER, W>(keys, len, tau, first, cand, K, o, sCnt);
   } else {
     const int n_eq = K - above_total;

@@ -48,6 +48,9 @@ def _dist(kind, shape, rng):
         return x
     if kind == "narrow":  # one binade: the first radix digit sees a single bin
         return (1.0 + rng.random(shape)).astype(np.float32)
+    if kind in ("sorted", "rsorted"):  # the largest keys at one end of the row
+        x = np.sort(rng.standard_normal(shape).astype(np.float32), axis=-1)
+        return np.ascontiguousarray(x[..., ::-1]) if kind == "rsorted" else x
     raise ValueError(kind)
 
 
@@ -115,14 +118,15 @@ def test_topk_workloads(name, nrows):
 
 
 @pytest.mark.parametrize("N", [40000, 65536, 70000], ids=["wide", "wide_max", "split"])
-@pytest.mark.parametrize("kind", ["special", "ties", "narrow"])
+@pytest.mark.parametrize("kind", ["special", "ties", "narrow", "normal", "sorted", "rsorted"])
 @pytest.mark.parametrize("K", [100, 2048, 4096])
 def test_topk_few_long_rows(kind, K, N):
     """Few rows with N > 8192.  N <= 65536: one 1024-thread workgroup per
     row with the row in registers (lengths straddle the 4096-key wave
-    segments).  N > 65536: every row is cut into 4096-key segments, one
-    workgroup each, that share the row's digit histograms (lengths straddle
-    segment boundaries)."""
+    segments; "sorted" and "rsorted" put the largest keys all in the last or
+    the first waves).  N > 65536: every row is cut into 4096-key segments,
+    one workgroup each, that share the row's digit histograms (lengths
+    straddle segment boundaries)."""
     rng = np.random.default_rng(K + len(kind) + N)
     B, M = 1, 10
     lg = _dist(kind, (B, M, N), rng)
