@@ -446,6 +446,74 @@ __device__ __forceinline__ int3 threshold_bin_n(const uint32_t* hist, int krem, 
   return make_int3(sSel[0], sSel[1], sSel[2]);
 }
 
+// One wave's search for the same bin of hist[0..NB) (NB a multiple of 256):
+// lane l sums its NB / 64 consecutive bins in groups of four, a wave scan
+// finds the lane holding the krem-th largest key, and that lane narrows it
+// to a group and then a bin.  Writes (bin, keys above it, its count) to
+// sSel; the caller's barrier publishes them.  One barrier per round instead
+// of two, for small bin counts (NB / 64 group sums stay in registers).
+template <int NB>
+__device__ __forceinline__ void threshold_wave(const uint32_t* hist, int krem, int* sSel) {
+  constexpr int BPL = NB / kWave, G = BPL / 4;
+  static_assert(BPL % 4 == 0, "groups of four bins");
+  const int lane = threadIdx.x & 63;
+  const uint4* hl = reinterpret_cast<const uint4*>(hist + lane * BPL);
+  int gs[G];
+  int tsum = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint4 x = hl[g];
+    gs[g] = (int)(x.x + x.y + x.z + x.w);
+    tsum += gs[g];
+  }
+  const int incl = wave_incl_scan(tsum);
+  int above = __builtin_amdgcn_readlane(incl, 63) - incl;  // keys in higher lanes' bins
+  if (above < krem && krem <= above + tsum) {  // exactly one lane
+    int gsel = 0, asel = 0;
+#pragma unroll
+    for (int g = G - 1; g >= 0; --g) {
+      if (above < krem && krem <= above + gs[g]) {
+        gsel = g;
+        asel = above;
+      }
+      above += gs[g];
+    }
+    const uint4 x = hl[gsel];
+    const int c[4] = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (asel < krem && krem <= asel + c[j]) {
+        sSel[0] = lane * BPL + 4 * gsel + j;
+        sSel[1] = asel;
+        sSel[2] = c[j];
+      }
+      asel += c[j];
+    }
+  }
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the wave's global loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A round's threshold after the histogram barrier: one wave for up to 2048
+// bins, all waves (threshold_bin_n) for more.
+template <int W, int NB>
+__device__ __forceinline__ int3 threshold_step(const uint32_t* hist, int krem, int* sRed,
+                                               int* sSel) {
+  if constexpr (NB <= 2048) {
+    if (wave_id() == 0) threshold_wave<NB>(hist, krem, sSel);
+    __syncthreads();
+    return make_int3(sSel[0], sSel[1], sSel[2]);
+  } else {
+    return threshold_bin_n<W, NB>(hist, krem, sRed, sSel);
+  }
+}
+
 // Digit layout of the 32-bit key: rounds of 11, 11 and 10 bits.
 __host__ __device__ constexpr int digit_bits(int round) { return round < 2 ? 11 : 10; }
 // Register-resident rows: a first digit of B0 bits, then the remaining
@@ -598,6 +666,13 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 #pragma unroll
     for (int c = 0; c < KR; ++c) keys[c] = order_key(v[c]);
   }
+  // both digit histograms are cleared while the loads are in flight
+  {
+    constexpr int nh = (1 << B0) + (1 << rdigit_bits(B0, 1));
+    for (int i = 4 * tid; i < nh; i += 4 * W * kWave)
+      *reinterpret_cast<uint4*>(hist + i) = make_uint4(0u, 0u, 0u, 0u);
+    lds_barrier();
+  }
   // only the wave that holds the row's end has slots past it (later waves
   // skip all their slots)
   if (base < len && len < base + SEG) mask_tail<KR>(keys, base + lane, len);
@@ -614,17 +689,22 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 #pragma unroll
   for (int round = 0; round < 3; ++round) {
     const int bits = rdigit_bits(B0, round), shift = rdigit_shift(B0, round);
+    // rounds 0 and 2 count into h0, round 1 into h1 (both cleared up front;
+    // h0 again during round 1)
+    uint32_t* h = round == 1 ? hist + (1 << B0) : hist;
     if (low_bits == 0) {
       const int nb = 1 << bits;
-      for (int i = tid; i < nb; i += W * kWave) hist[i] = 0u;
-      __syncthreads();
+      if (round == 1) {
+        constexpr int nb2 = 1 << rdigit_bits(B0, 2);
+        for (int i = tid; i < nb2; i += W * kWave) hist[i] = 0u;
+      }
 #pragma unroll
       for (int c = 0; c < KR; ++c) {
         // wave-uniform: the rest of the segment is empty
         if (c % kChunk == 0 && base + c * kWave >= len) break;
         const uint32_t u = keys[c];
         if (round == 0) {
-          atomicAdd(&hist[u >> shift], one);
+          atomicAdd(&h[u >> shift], one);
         } else if (shift != 0) {
           // the keys under the prefix are those whose digit offset
           // (u >> shift) - (prefix << bits) is below nb; as a byte offset,
@@ -632,20 +712,23 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
           const uint32_t a = (__builtin_amdgcn_ubfe(u, shift, 32 - shift) << 2) -
                              (prefix << (bits + 2));
           if (a < (uint32_t)(4 * nb))
-            atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + a), one);
+            atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(h) + a), one);
         } else {
           const uint32_t d = u - (prefix << bits);
-          if (d < (uint32_t)nb) atomicAdd(&hist[d], one);
+          if (d < (uint32_t)nb) atomicAdd(&h[d], one);
         }
       }
       __syncthreads();
       int3 sel;
-      if (round == 0)
-        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 0)>(hist, krem, sRed, sSel);
-      else if (round == 1)
-        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 1)>(hist, krem, sRed, sSel);
-      else
-        sel = threshold_bin_n<W, 1 << rdigit_bits(B0, 2)>(hist, krem, sRed, sSel);
+      constexpr int nb0 = 1 << rdigit_bits(B0, 0), nb1 = 1 << rdigit_bits(B0, 1),
+                    nb2 = 1 << rdigit_bits(B0, 2);
+      if (round == 0) {
+        sel = threshold_step<W, nb0>(h, krem, sRed, sSel);
+      } else if (round == 1) {
+        sel = threshold_step<W, nb1>(h, krem, sRed, sSel);
+      } else {
+        sel = threshold_step<W, nb2>(h, krem, sRed, sSel);
+      }
       prefix = (prefix << bits) | (uint32_t)sel.x;
       krem -= sel.y;
       above_total += sel.y;
@@ -665,7 +748,7 @@ __device__ __forceinline__ void row_select(const float* __restrict__ src,
 }
 
 #define DSA_TOPK_LDS                                  \
-  __shared__ __align__(16) uint32_t hist[2048];       \
+  __shared__ __align__(16) uint32_t hist[4096];       \
   __shared__ int sRed[kRowWaves];                     \
   __shared__ int sSel[3];                             \
   __shared__ int sCnt[2][kRowWaves];
@@ -678,7 +761,7 @@ __global__ __launch_bounds__(W * kWave) void topk_row_kernel(const float* __rest
                                                              const int* __restrict__ ks,
                                                              const int* __restrict__ ke,
                                                              int* __restrict__ out, int N, int K) {
-  __shared__ __align__(16) uint32_t hist[1 << (B0 > 11 ? B0 : 11)];
+  __shared__ __align__(16) uint32_t hist[(1 << B0) + (1 << rdigit_bits(B0, 1))];
   __shared__ int sRed[W];
   __shared__ int sSel[3];
   __shared__ int sCnt[2][W];
