@@ -285,21 +285,22 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     i32x4* pre = pre2[SET];
     float& pks = pks2[SET];
     const int kb = c0 + tile * C::KT;
+    // Every load is issued and its data used as loaded: a key past the
+    // range reads the range's last key, whose score column is computed but
+    // never stored.  So nothing waits on a load before the tile's LDS store,
+    // and the number of loads in flight does not depend on the data (the
+    // wait before that store leaves the next tile's loads outstanding).
 #pragma unroll
     for (int j = 0; j < C::CPT; ++j) {
       const int ch = tid + j * kIdxThreads;
       i32x4 v = {0, 0, 0, 0};
-      if (ch < C::CHUNKS) {
-        const int key = kb + ch / C::CPR;
-        if (key < c1)
-          v = *reinterpret_cast<const i32x4*>(k + ((size_t)b * N + key) * D + (ch % C::CPR) * 16);
+      if (C::CHUNKS % kIdxThreads == 0 || ch < C::CHUNKS) {
+        const int key = min(kb + ch / C::CPR, c1 - 1);
+        v = *reinterpret_cast<const i32x4*>(k + ((size_t)b * N + key) * D + (ch % C::CPR) * 16);
       }
       pre[j] = v;
     }
-    if (tid < C::KT) {
-      const int key = kb + tid;
-      pks = key < c1 ? k_scale[(size_t)b * N + key] : 0.f;
-    }
+    if (C::KT >= kIdxThreads || tid < C::KT) pks = k_scale[(size_t)b * N + min(kb + tid, c1 - 1)];
   };
   auto lstore = [&](auto setc) {
     constexpr int SET = decltype(setc)::value;
@@ -309,16 +310,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
 #pragma unroll
     for (int j = 0; j < C::CPT; ++j) {
       const int ch = tid + j * kIdxThreads;
-      if (ch < C::CHUNKS)
+      if (C::CHUNKS % kIdxThreads == 0 || ch < C::CHUNKS)
         *reinterpret_cast<i32x4*>(&sK[buf][tile_off<D>(ch / C::CPR, ch % C::CPR)]) = pre[j];
     }
-    if (tid < C::KT) sKs[buf][tid] = pks;
+    if (C::KT >= kIdxThreads || tid < C::KT) sKs[buf][tid] = pks;
   };
 
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
   gload(0, Set0{});
-  if (ntiles > 1) gload(1, Set1{});
+  gload(ntiles > 1 ? 1 : 0, Set1{});
   lstore(Set0{});
   __syncthreads();
 
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
     constexpr int SET = decltype(setc)::value;
     constexpr int buf = SET;
     const int kb = c0 + tile * C::KT;
-    if (tile + 2 < ntiles) gload(tile + 2, setc);
+    gload(tile + 2 < ntiles ? tile + 2 : ntiles - 1, setc);  // the last tile again at the end
     // skip waves whose tokens do not see this tile
     if (wmax > kb && wmin < kb + C::KT) {
       // 16-key sub-tiles, software pipelined (128-deep keys): the MFMAs of
