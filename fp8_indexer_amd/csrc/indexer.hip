@@ -44,6 +44,10 @@ constexpr int kKT = DSA_IDX_KT;                 // keys per LDS tile (tuning kno
 constexpr int kXcds = 8;
 constexpr int kMinChunk = 64;   // keys per chunk, at least (one key tile)
 constexpr int kBalBlocks = 1024;  // key-parallel: token blocks of the balanced schedule, at most
+#ifndef DSA_IDX_PIECE_OV
+#define DSA_IDX_PIECE_OV 512
+#endif
+constexpr int kPieceOv = DSA_IDX_PIECE_OV;  // balanced schedule: start-up cost of a piece, in keys
 // VALU instructions scheduled after each MFMA of the next sub-tile (tuning knob)
 #ifndef DSA_IDX_VPM
 #define DSA_IDX_VPM 10
@@ -464,7 +468,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
           }
         }
       }
-      len[j] = emax > smin ? emax - smin : 0;
+      // a piece costs its keys plus a start-up (q, weights, the first key
+      // tiles' latency) worth about kPieceOv keys: the schedule counts it
+      len[j] = emax > smin ? emax - smin + kPieceOv : 0;
       tsum += len[j];
     }
     // exclusive prefix of the block lengths in sCum[0..nblk], sCum[nblk] =
@@ -507,8 +513,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_logits_kernel(
       const int b0 = sCum[i], b1 = sCum[i + 1];
       if (b1 <= pos) continue;  // an empty block
       const int stop = min(end, b1);
-      __syncthreads();  // the previous piece's LDS reads are complete
-      process(i / n_tblocks, i % n_tblocks, pos - b0, stop - b0);
+      // the block's keys follow its start-up share [b0, b0 + kPieceOv)
+      const int k0 = max(pos - b0 - kPieceOv, 0), k1 = stop - b0 - kPieceOv;
+      if (k1 > k0) {
+        __syncthreads();  // the previous piece's LDS reads are complete
+        process(i / n_tblocks, i % n_tblocks, k0, k1);
+      }
       pos = stop;
     }
   } else {
@@ -559,7 +569,7 @@ hipError_t launch_kp(const IndexerArgs& a, hipStream_t stream) {
   const int n_chunks = (int)((a.N + chunk_keys - 1) / chunk_keys);
   const long long items = tblocks * n_chunks;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (KP && tblocks <= kBalBlocks && tblocks * a.N <= 0x7fffffffLL) {
+  if (KP && tblocks <= kBalBlocks && tblocks * (a.N + kPieceOv) <= 0x7fffffffLL) {
     // key-parallel, balanced over the device-side windows (n_chunks = 0)
     hipLaunchKernelGGL((indexer_logits_kernel<H, D, KP, RT>), dim3((unsigned)slots),
                        dim3(kIdxThreads), 0, stream, (const uint8_t*)a.q, a.q_scale,
