@@ -671,22 +671,48 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   }
   if constexpr (SPLIT) {
     // split: this split's normalised O in bf16 (O / l; 0 without a valid
-    // index) and (m, l) of each head, for the merge kernel
+    // index) into the workspace, staged through LDS as in the unsplit
+    // epilogue below (whole 16-byte lanes of each head row), and (m, l) of
+    // each head, for the merge kernel
     const size_t part = (size_t)rtok * S + split;
+    constexpr int OS = DV + 8;
+    constexpr int OP = (NW * HPW * OS * 2 + (int)sizeof(sKV) - 1) / (int)sizeof(sKV);
+    constexpr int ORP = NW * HPW / OP;  // head rows per pass
+    static_assert((NW * HPW) % OP == 0 && ORP * OS * 2 <= (int)sizeof(sKV), "O staging");
+    uint16_t* so = &sKV[0][0];
+    const int ln = fresh_lane_id(), colx = ln & 15, gx = ln >> 4;
+    float inv[OH];
 #pragma unroll
     for (int oh = 0; oh < OH; ++oh) {
-      const int h = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 + col;
-      uint16_t* orow = wso + (part * Hq + h) * DV + c0 + g * 4;
-      const float inv = lf[oh] > 0.f ? __builtin_amdgcn_rcpf(lf[oh]) : 0.f;
+      const int h = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 + colx;
+      if (gx == 0 && wave % PG == 0) wsml[part * Hq + h] = float2{mf[oh], lf[oh]};
+      inv[oh] = lf[oh] > 0.f ? __builtin_amdgcn_rcpf(lf[oh]) : 0.f;
+    }
 #pragma unroll
-      for (int t = 0; t < OTW; ++t) {
-        const f32x4 v = oacc[oh][t];
-        uint2 pk2;
-        pk2.x = pack_bf16x2(v[0] * inv, v[1] * inv);
-        pk2.y = pack_bf16x2(v[2] * inv, v[3] * inv);
-        *reinterpret_cast<uint2*>(orow + t * 16) = pk2;
+    for (int pass = 0; pass < OP; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's rows are read
+#pragma unroll
+      for (int oh = 0; oh < OH; ++oh) {
+        const int hr = ((wave / PG) * PG + pgrp(oh)) * HPW + (oh % HT) * 16 - pass * ORP;
+        if (hr >= 0 && hr < ORP) {  // uniform over the wave
+          uint16_t* srow = so + (hr + colx) * OS + c0 + gx * 4;
+#pragma unroll
+          for (int t = 0; t < OTW; ++t) {
+            const f32x4 v = oacc[oh][t] * inv[oh];
+            uint2 pk2;
+            pk2.x = pack_bf16x2(v[0], v[1]);
+            pk2.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(srow + t * 16) = pk2;
+          }
+        }
       }
-      if (g == 0 && wave % PG == 0) wsml[part * Hq + h] = float2{mf[oh], lf[oh]};
+      __syncthreads();
+      uint16_t* obase = wso + (part * Hq + pass * ORP) * DV;
+      for (int u = tid; u < ORP * (DV / 8); u += C::THREADS) {
+        const int r = u / (DV / 8), c8 = u % (DV / 8);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * DV + c8 * 8) =
+            *reinterpret_cast<const i32x4*>(so + r * OS + c8 * 8);
+      }
     }
   } else {
     // Normalised bf16 O goes through LDS (the KV tile buffers, free now) in
