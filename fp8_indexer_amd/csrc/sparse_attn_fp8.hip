@@ -646,22 +646,40 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
     inv[oh] = l > 0.f ? __builtin_amdgcn_rcpf(l * pf_out) : 0.f;
   }
   if constexpr (SPLIT) {
-    // this split's O / l in bf16 (0 without a valid index), straight from
-    // the C layout: lane (h, g) holds columns c0 + 32t + 8i + 4g + j
+    // this split's O / l in bf16 (0 without a valid index) into the
+    // workspace, staged through LDS as in the unsplit epilogue below
     const size_t part = (size_t)rtok * S + split;
+    constexpr int OS = kDv + 8;
+    constexpr int ORP = 64;
+    static_assert(ORP * OS * 2 <= 2 * kTile, "O staging");
+    uint16_t* so = reinterpret_cast<uint16_t*>(&sKV[0][0]);
 #pragma unroll
-    for (int oh = 0; oh < NHT; ++oh) {
-      uint16_t* orow = wso + (part * HQ + oh * 32 + hl) * kDv + c0 + 4 * g;
+    for (int pass = 0; pass < HQ / ORP; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's rows are read
 #pragma unroll
-      for (int t = 0; t < kOTW; ++t)
+      for (int oh = 0; oh < NHT; ++oh) {
+        const int hr = oh * 32 - pass * ORP;
+        if (hr >= 0 && hr < ORP) {
+          uint16_t* srow = so + (hr + hl) * OS + c0 + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x16& v = oacc[oh][t];
-          uint2 pk2;
-          pk2.x = pack_bf16x2(v[4 * i] * inv[oh], v[4 * i + 1] * inv[oh]);
-          pk2.y = pack_bf16x2(v[4 * i + 2] * inv[oh], v[4 * i + 3] * inv[oh]);
-          *reinterpret_cast<uint2*>(orow + 32 * t + 8 * i) = pk2;
+          for (int t = 0; t < kOTW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x16& v = oacc[oh][t];
+              uint2 pk2;
+              pk2.x = pack_bf16x2(v[4 * i] * inv[oh], v[4 * i + 1] * inv[oh]);
+              pk2.y = pack_bf16x2(v[4 * i + 2] * inv[oh], v[4 * i + 3] * inv[oh]);
+              *reinterpret_cast<uint2*>(srow + 32 * t + 8 * i) = pk2;
+            }
         }
+      }
+      __syncthreads();
+      uint16_t* obase = wso + (part * HQ + pass * ORP) * kDv;
+      for (int u = tid; u < ORP * (kDv / 8); u += kThreads) {
+        const int r = u / (kDv / 8), c8 = u % (kDv / 8);
+        *reinterpret_cast<i32x4*>(obase + (size_t)r * kDv + c8 * 8) =
+            *reinterpret_cast<const i32x4*>(so + r * OS + c8 * 8);
+      }
     }
   } else {
     // bf16 O through LDS (the KV buffers, free now) in passes of 64 heads so
