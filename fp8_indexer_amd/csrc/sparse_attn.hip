@@ -769,38 +769,47 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
 // columns): o = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s + e^sink 2^-M)
 // with M = max_s m_s -- the same value as one pass over all K indices,
 // since every split's O_s and l_s share its reference m_s.
-template <int DV>
+template <int DV, int CW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const uint16_t* __restrict__ wso,
                                                          const float2* __restrict__ wsml,
                                                          const float* __restrict__ sink,
                                                          uint16_t* __restrict__ o, int Hq, int S) {
-  constexpr int TPH = DV / 4;        // threads per head
+  // CW output columns per thread (8: one 16-byte load per split)
+  static_assert(CW == 4 || CW == 8, "columns per thread");
+  constexpr int TPH = DV / CW;       // threads per head
   constexpr int HPB = 256 / TPH;     // heads per workgroup
   static_assert(256 % TPH == 0, "DV");
+  using pk_t = std::conditional_t<CW == 8, uint4, uint2>;
   const int hblocks = Hq / HPB;
   const int row = blockIdx.x / hblocks;
   const int h = (blockIdx.x % hblocks) * HPB + threadIdx.x / TPH;
-  const int cq = (threadIdx.x % TPH) * 4;
+  const int cq = (threadIdx.x % TPH) * CW;
   const size_t p0 = (size_t)row * S;
   float mmax = -INFINITY;
   for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, wsml[(p0 + s) * Hq + h].x);
   float l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) acc[j] = 0.f;
   for (int s = 0; s < S; ++s) {
     const float2 ml = wsml[(p0 + s) * Hq + h];
     const float wgt = fast_exp2(ml.x - mmax) * ml.y;  // the split's share of l
     l += wgt;
-    const uint2 pk = *reinterpret_cast<const uint2*>(wso + ((p0 + s) * Hq + h) * DV + cq);
-    acc += wgt * f32x4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xffff0000u),
-                       __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xffff0000u)};
+    const pk_t pk = *reinterpret_cast<const pk_t*>(wso + ((p0 + s) * Hq + h) * DV + cq);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&pk);
+#pragma unroll
+    for (int j = 0; j < CW / 2; ++j) {
+      acc[2 * j] += wgt * __uint_as_float(w[j] << 16);
+      acc[2 * j + 1] += wgt * __uint_as_float(w[j] & 0xffff0000u);
+    }
   }
   if (sink) l += fast_exp2(sink[h] * kLog2e - mmax);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const f32x4 v = acc * inv;
-  uint2 pk2;
-  pk2.x = pack_bf16x2(v[0], v[1]);
-  pk2.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<uint2*>(o + ((size_t)row * Hq + h) * DV + cq) = pk2;
+  pk_t out;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&out);
+#pragma unroll
+  for (int j = 0; j < CW / 2; ++j) w[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  *reinterpret_cast<pk_t*>(o + ((size_t)row * Hq + h) * DV + cq) = out;
 }
 
 // Splits of each row's K indices: with few rows (decode: B*M at most half
@@ -886,14 +895,14 @@ hipError_t launch_attn_merge(const uint16_t* wso, const float2* wsml, const floa
                              uint16_t* o, long long rows, int Hq, int Dv, int S,
                              hipStream_t stream) {
   if (Dv == 512) {
-    constexpr int HPB = 256 / (512 / 4);
+    constexpr int HPB = 256 / (512 / 8);
     if (Hq % HPB != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_merge_kernel<512>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
+    hipLaunchKernelGGL((attn_merge_kernel<512, 8>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
                        0, stream, wso, wsml, sink, o, Hq, S);
   } else if (Dv == 64) {
     constexpr int HPB = 256 / (64 / 4);
     if (Hq % HPB != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_merge_kernel<64>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
+    hipLaunchKernelGGL((attn_merge_kernel<64, 4>), dim3((unsigned)(rows * (Hq / HPB))), dim3(256),
                        0, stream, wso, wsml, sink, o, Hq, S);
   } else {
     return hipErrorInvalidValue;
