@@ -48,4 +48,20 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Split launches (S workgroups per row, row = blockIdx / S, split =
+// blockIdx % S): when the row count is a multiple of the 8 XCDs, remap so
+// that the S splits of a row run on one XCD.  Workgroups are dealt to the
+// XCDs in turn (workgroup g on XCD g % 8), so the row's q, which every split
+// reads, comes from HBM once and from that XCD's L2 for the others.  The map
+// is a bijection of (row, split) pairs whatever the placement.
+__device__ __forceinline__ void split_to_xcd(int& row, int& split, int S) {
+  constexpr int kXcd = 8;
+  const int g = (int)blockIdx.x, rows = (int)gridDim.x / S;
+  if (S > 1 && rows % kXcd == 0) {
+    const int j = g / kXcd;  // position among the workgroups of XCD g % 8
+    row = (j / S) * kXcd + g % kXcd;
+    split = j % S;
+  }
+}
+
 }  // namespace dsa

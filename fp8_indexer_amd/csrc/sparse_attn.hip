@@ -192,8 +192,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
   const int g = lane >> 4, col = lane & 15;
   // workgroup -> (b, t) row, latest first, and split s of its K indices:
   // [s*kspan, s*kspan + klen) (S = 1: the whole row)
-  const int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
-  const int split = (int)(blockIdx.x % S);
+  int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
+  int split = (int)(blockIdx.x % S);
+  if constexpr (SPLIT) {
+    int rrow = (int)(blockIdx.x / S);
+    split_to_xcd(rrow, split, S);
+    rtok = (int)(gridDim.x / S) - 1 - rrow;
+  }
   const int b = rtok / M;
   const int kbeg = split * kspan;
   const int klen = max(0, min(K - kbeg, kspan));

@@ -203,8 +203,14 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_fp8_kernel(
   const int hq = qht * 32 + hl;              // this lane's head in QK^T / softmax
   const int c0 = wave * (kDv / 4);           // first output column of this wave's PV
 
-  const int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
-  const int split = (int)(blockIdx.x % S);
+  // workgroup -> (b, t) row, latest first, and split s of its K indices
+  int rtok = (int)(gridDim.x / S - 1 - blockIdx.x / S);
+  int split = (int)(blockIdx.x % S);
+  if constexpr (SPLIT) {
+    int rrow = (int)(blockIdx.x / S);
+    split_to_xcd(rrow, split, S);
+    rtok = (int)(gridDim.x / S) - 1 - rrow;
+  }
   const int b = rtok / M;
   const int kbeg = split * kspan;
   const int klen = max(0, min(K - kbeg, kspan));
