@@ -12,10 +12,13 @@
 //   dsink -= p_sink Delta
 //
 // Design (MI355X-first):
-//  * One workgroup per (query token, group of 16 heads), 4 waves that take
-//    the token's 16-row tiles in turn (wave w: tiles w, w+4, ...), each
-//    gathering its own tiles into its own LDS buffer, so the waves never
-//    wait for each other inside the loops.
+//  * One workgroup per (query token, group of 16 heads).  The token's
+//    indices go to LDS once, with the list of its 16-row tiles that hold a
+//    valid index (the others are skipped); 4 waves take the listed tiles in
+//    turn (wave w: entries w, w+4, ...), each gathering its own tiles into
+//    its own LDS buffer, so the waves never wait for each other inside the
+//    loops.  The rows of a wave's next tile are loaded into registers while
+//    it computes the current one.
 //  * Pass 1 recomputes lse: S^T = KV.Q^T on v_mfma_f32_16x16x32_bf16 (q
 //    B-fragments in VGPRs), an online max / sum per head, combined over the
 //    lane groups and the waves, with the sink.
@@ -28,9 +31,11 @@
 //      dkv   = [scale dS | P] [q ; dO] on v_mfma_f32_16x16x32_bf16 with the
 //               16 heads of dS and the 16 heads of P as the 32-deep k
 //               dimension: A from a small LDS transpose of dS and P, B read
-//               transposed from q and dO in LDS; each 16x16 block is added to
-//               the gathered rows of dkv with fp32 atomics (rows repeat across
-//               tokens: the scatter of the pages' backward).
+//               transposed from q and dO in LDS; the blocks are added to the
+//               gathered rows of dkv with fp32 atomics (rows repeat across
+//               tokens: the scatter of the pages' backward), two column
+//               tiles at a time rearranged by a lane swap so that each
+//               atomic instruction covers whole 128-byte lines.
 //  * dq, dkv and dsink accumulate in fp32 (dq and dsink with atomics over
 //    the waves and head groups); the entry point zero-fills them first.
 //  * Invalid indices (-1 or outside [0, N)) gather nothing, have p = 0 and
@@ -42,6 +47,7 @@ namespace dsa {
 namespace {
 
 constexpr float kLog2eB = 1.4426950408889634f;
+constexpr int kMaxKB = 4096;  // largest supported top-k
 
 typedef short bs4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -91,7 +97,9 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   __shared__ __align__(16) uint16_t sQ[16 * RS];
   __shared__ __align__(16) uint16_t sG[16 * GS];
   __shared__ __align__(16) uint16_t sT[NW][TR * C::TS];
-  __shared__ int sIdx[NW][TR];
+  __shared__ int sIdx[kMaxKB];            // the row's indices, -1 if invalid
+  __shared__ int sList[kMaxKB / TR];      // tiles holding a valid index
+  __shared__ int sCnt[NW], sNvt;
   __shared__ float sM[NW][16], sL[NW][16], sDelta[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -102,10 +110,17 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   const int h0 = (int)(blockIdx.x % hgs) * 16;     // first head of the group
   const int b = r / M;
   const int* ridx = idx + (size_t)r * K;
-  const int ntiles = (K + TR - 1) / TR;
+  const int ntiles = (K + TR - 1) / TR;  // <= THREADS (K <= kMaxKB)
 
-  // ---- q and dO rows of the 16 heads into LDS; Delta = dO . o per head ----
+  // ---- the row's indices, q and dO of the 16 heads into LDS; Delta = dO . o
+  // per head -------------------------------------------------------------------
   {
+    // invalid indices (-1 or outside [0, N)) and the padding of the last
+    // tile read as -1
+    for (int p = tid; p < ntiles * TR; p += C::THREADS) {
+      const int v = p < K ? ridx[p] : -1;
+      sIdx[p] = (v >= 0 && v < N) ? v : -1;
+    }
     const uint16_t* qg = q + ((size_t)r * Hq + h0) * DQK;
     for (int u = tid; u < 16 * (DQK / 8); u += C::THREADS) {
       const int hh = u / (DQK / 8), c8 = u % (DQK / 8);
@@ -130,6 +145,26 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     if (col == 0) sDelta[hh] = acc;
   }
   __syncthreads();
+  // list of the tiles that hold a valid index, in order (one thread per tile)
+  {
+    bool any = false;
+    if (tid < ntiles)
+#pragma unroll
+      for (int i = 0; i < TR; ++i) any = any || sIdx[tid * TR + i] >= 0;
+    const uint64_t m = __ballot(any);
+    if (lane == 0) sCnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      off += w < wave ? sCnt[w] : 0;
+      tot += sCnt[w];
+    }
+    if (any) sList[off + __popcll(m & ((1ull << lane) - 1ull))] = tid;
+    if (tid == 0) sNvt = tot;
+  }
+  __syncthreads();
+  const int nvt = sNvt;
 
   // q B-fragments (S^T = KV.Q^T): head col, k-step c: columns 32c + 8g..+7
   bf16x8 qf[C::KC];
@@ -137,36 +172,44 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   for (int c = 0; c < C::KC; ++c)
     qf[c] = *reinterpret_cast<const bf16x8*>(&sQ[col * RS + c * 32 + g * 8]);
 
-  // ---- gathering a tile: 16 rows of this wave's tile `it` into sKV[wave] ----
+  // ---- gathering: wave w takes list entries w, w + NW, ...; the rows of its
+  // next tile are loaded into registers while it computes the current one
+  // (invalid slots load row 0 of the batch entry: finite data whose p and ds
+  // are 0), so every load is issued unconditionally
   uint16_t* kvt = sKV[wave];
-  auto stage = [&](int it) {
-    if (lane < TR) {
-      const int p = it * TR + lane;
-      const int v = p < K ? ridx[p] : -1;
-      sIdx[wave][lane] = (v >= 0 && v < N) ? v : -1;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // invalid slots gather row 0 of the batch entry (finite data; their p
-    // and ds are 0 and their dkv is not written), so every load is issued
-    // unconditionally, before the first wait
-    static_assert(C::CPL * kWave == TR * C::CPR, "whole chunks per lane");
-    i32x4 buf[C::CPL];
+  static_assert(C::CPL * kWave == TR * C::CPR, "whole chunks per lane");
+  i32x4 nb[C::CPL];
+  auto issue = [&](int e) {
+    const int* ti = sIdx + sList[e] * TR;
 #pragma unroll
     for (int k = 0; k < C::CPL; ++k) {
       const int ch = lane + k * kWave;
-      const int j = max(sIdx[wave][ch / C::CPR], 0);
-      buf[k] = *reinterpret_cast<const i32x4*>(kv + ((size_t)b * N + j) * DQK + (ch % C::CPR) * 8);
+      const int j = max(ti[ch / C::CPR], 0);
+      nb[k] = *reinterpret_cast<const i32x4*>(kv + ((size_t)b * N + j) * DQK + (ch % C::CPR) * 8);
     }
+  };
+  auto commit = [&]() {
 #pragma unroll
     for (int k = 0; k < C::CPL; ++k) {
       const int ch = lane + k * kWave;
-      *reinterpret_cast<i32x4*>(&kvt[(ch / C::CPR) * RS + (ch % C::CPR) * 8]) = buf[k];
+      *reinterpret_cast<i32x4*>(&kvt[(ch / C::CPR) * RS + (ch % C::CPR) * 8]) = nb[k];
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+  // one pass over this wave's tiles; the last iteration reloads its own
+  // tile (never stored) so that the loads are unconditional
+  auto over_tiles = [&](auto&& body) {
+    if (wave < nvt) issue(wave);
+    for (int e = wave; e < nvt; e += NW) {
+      commit();
+      __builtin_amdgcn_wave_barrier();
+      issue(e + NW < nvt ? e + NW : e);
+      body(sIdx + sList[e] * TR);
+      __builtin_amdgcn_wave_barrier();  // kvt is read until here
+    }
   };
   // S^T of the current tile in the C layout: lane (col = head, g) holds rows
   // 4g + i; scores in log2 units, -inf for invalid rows
-  auto scores = [&](float (&s2)[4]) {
+  auto scores = [&](const int* ti, float (&s2)[4]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
@@ -175,15 +218,14 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      s2[i] = sIdx[wave][4 * g + i] >= 0 ? acc[i] * scale_log2 : -INFINITY;
+      s2[i] = ti[4 * g + i] >= 0 ? acc[i] * scale_log2 : -INFINITY;
   };
 
   // ---- pass 1: lse per head (log2 units) ------------------------------------
   float mrun = -INFINITY, lrun = 0.f;  // per lane: its head, its rows
-  for (int it = wave; it < ntiles; it += NW) {
-    stage(it);
+  over_tiles([&](const int* ti) {
     float s2[4];
-    scores(s2);
+    scores(ti, s2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (s2[i] == -INFINITY) continue;  // invalid row
@@ -193,7 +235,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
       }
       lrun += fast_exp2(s2[i] - mrun);
     }
-  }
+  });
   // combine the four lane groups of each head, then the waves
 #pragma unroll
   for (int m = 16; m <= 32; m <<= 1) {
@@ -234,10 +276,9 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   uint16_t* st = sT[wave];
   // transposing-read offsets: 4x16 blocks, lane (col) -> row col/4, column 4(col%4)
   const int trr = col >> 2, trc = 4 * (col & 3);
-  for (int it = wave; it < ntiles; it += NW) {
-    stage(it);
+  over_tiles([&](const int* ti) {
     float s2[4];
-    scores(s2);
+    scores(ti, s2);
     // dP^T = V.dO^T
     f32x4 dpa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -271,15 +312,11 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     __builtin_amdgcn_wave_barrier();
     // dkv[j, d] = sum_k A[j, k] B[k, d]: A row col, k = 8g..8g+7
     const bf16x8 aT = *reinterpret_cast<const bf16x8*>(&st[col * C::TS + 8 * g]);
-    int jrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) jrow[i] = sIdx[wave][4 * g + i];
-#pragma unroll 4
-    for (int t = 0; t < C::DT; ++t) {
-      // B row block k = 8g..8g+7: q heads (g < 2) or dO heads (g >= 2), column
-      // 16t + col; two transposing reads of 4 heads each
-      // (every lane reads; the dO columns past Dv are read in range and
-      // replaced by zeros)
+    // B row block k = 8g..8g+7 of column tile t: q heads (g < 2) or dO heads
+    // (g >= 2), column 16t + col; two transposing reads of 4 heads each
+    // (every lane reads; the dO columns past Dv are read in range and
+    // replaced by zeros)
+    auto dkv_tile = [&](int t) {
       const bool from_q = g < 2;
       const uint16_t* bp = from_q ? &sQ[(8 * g + trr) * RS + 16 * t + trc]
                                   : &sG[(8 * (g - 2) + trr) * GS +
@@ -292,15 +329,39 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
       }
       const bf16x8 bB = __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0],
                                                           hi[1], hi[2], hi[3]});
-      const f32x4 c = mfma_bf16_16x16x32(aT, bB, f32x4{0.f, 0.f, 0.f, 0.f});
-      // C: column 16t + col, rows 4g + i
+      return mfma_bf16_16x16x32(aT, bB, f32x4{0.f, 0.f, 0.f, 0.f});
+    };
+    // The C tiles of column tiles t and t+1 hold, in lane (g, col), rows
+    // 4g + i at column col of each.  One v_permlane16_swap per i (the odd
+    // 16-lane groups of tile t exchanged with the even ones of tile t+1)
+    // turns them into two
+    // sets of 2 rows x 32 consecutive columns: groups 0, 1 hold row 8(g/2) + i
+    // (first result) or 8(g/2) + 4 + i (second), at column 16t + 16(g%2) +
+    // col.  Each atomic instruction then covers two whole 128-byte lines of
+    // dkv instead of four half lines.
+    static_assert(C::DT % 2 == 0, "column tiles in pairs");
+    int jA[4], jB[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (jrow[i] >= 0)
-          unsafeAtomicAdd(dkv + ((size_t)b * N + jrow[i]) * DQK + 16 * t + col, c[i]);
+    for (int i = 0; i < 4; ++i) {
+      jA[i] = ti[8 * (g >> 1) + i];
+      jB[i] = ti[8 * (g >> 1) + 4 + i];
     }
-    __builtin_amdgcn_wave_barrier();  // st and the tile are reused next tile
-  }
+    float* dk = dkv + (size_t)b * N * DQK + 16 * (g & 1) + col;
+#pragma unroll
+    for (int t = 0; t < C::DT; t += 2) {
+      const f32x4 c0 = dkv_tile(t), c1 = dkv_tile(t + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // (element values through __float_as_uint: a bit cast of a vector
+        // element reads element 0 whatever the index)
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(c0[i]),
+                                                        __float_as_uint(c1[i]), false, false);
+        const float va = __uint_as_float(sw[0]), vb = __uint_as_float(sw[1]);
+        if (jA[i] >= 0) unsafeAtomicAdd(dk + (size_t)jA[i] * DQK + 16 * t, va);
+        if (jB[i] >= 0) unsafeAtomicAdd(dk + (size_t)jB[i] * DQK + 16 * t, vb);
+      }
+    }
+  });
   // dq of this wave's tiles (the waves' partial sums are added atomically)
   float* dqr = dq + ((size_t)r * Hq + h0 + col) * DQK;
 #pragma unroll
