@@ -85,7 +85,12 @@ struct BwdCfg {
   static constexpr int TS = 40;           // row stride of the dS|P transpose (elements)
 };
 
-template <int DQK, int DV>
+// NH = 1: one workgroup per (token, 16 heads), each wave alone on its own
+// tiles.  NH = 2: one workgroup per (token, 32 heads); waves w and w + 2
+// (heads 0-15 and 16-31 of the group) share each gathered tile, and each
+// adds to dkv half of the columns, summed over all 32 heads: half the fp32
+// atomics and half the gathers of NH = 1.
+template <int DQK, int DV, int NH>
 __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const float* __restrict__ sink, const int* __restrict__ idx, const uint16_t* __restrict__ o,
@@ -93,27 +98,36 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     float* __restrict__ dsink, int M, int N, int Hq, int K, float scale, float scale_log2) {
   using C = BwdCfg<DQK, DV>;
   constexpr int NW = C::NW, TR = C::TR, RS = C::RS, GS = C::GS;
-  __shared__ __align__(16) uint16_t sKV[NW][TR * RS];
-  __shared__ __align__(16) uint16_t sQ[16 * RS];
-  __shared__ __align__(16) uint16_t sG[16 * GS];
+  constexpr int HG = 16 * NH;       // heads per workgroup
+  constexpr int NS = NW / NH;       // tile streams, NH waves each
+  constexpr int CPW = C::CPL / NH;  // gather chunks per lane and wave
+  constexpr int DTW = C::DT / NH;   // dkv column tiles per wave
+  static_assert(NH == 1 || NH == 2, "head halves");
+  static_assert(CPW * NH == C::CPL && DTW * NH == C::DT && DTW % 2 == 0, "splits");
+  __shared__ __align__(16) uint16_t sKV[NS][TR * RS];
+  __shared__ __align__(16) uint16_t sQ[HG * RS];
+  __shared__ __align__(16) uint16_t sG[HG * GS];
   __shared__ __align__(16) uint16_t sT[NW][TR * C::TS];
   __shared__ int sIdx[kMaxKB];            // the row's indices, -1 if invalid
   __shared__ int sList[kMaxKB / TR];      // tiles holding a valid index
   __shared__ int sCnt[NW], sNvt;
-  __shared__ float sM[NW][16], sL[NW][16], sDelta[16];
+  __shared__ float sM[NW][16], sL[NW][16], sDelta[HG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, col = lane & 15;
-  const int hgs = Hq / 16;
+  // tile stream and head half (compile-time 0 for NH = 1)
+  const int stream = NH == 1 ? wave : wave % NS, hl = NH == 1 ? 0 : wave / NS;
+  const int hgs = Hq / HG;
   const int r = (int)(blockIdx.x / hgs);           // (b, t) row
-  const int h0 = (int)(blockIdx.x % hgs) * 16;     // first head of the group
+  const int h0 = (int)(blockIdx.x % hgs) * HG;     // first head of the group
+  const int hw = 16 * hl;                          // this wave's heads: h0 + hw + 0..15
   const int b = r / M;
   const int* ridx = idx + (size_t)r * K;
   const int ntiles = (K + TR - 1) / TR;  // <= THREADS (K <= kMaxKB)
 
-  // ---- the row's indices, q and dO of the 16 heads into LDS; Delta = dO . o
-  // per head -------------------------------------------------------------------
+  // ---- the row's indices, q and dO of the group's heads into LDS; Delta =
+  // dO . o per head ------------------------------------------------------------
   {
     // invalid indices (-1 or outside [0, N)) and the padding of the last
     // tile read as -1
@@ -122,27 +136,30 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
       sIdx[p] = (v >= 0 && v < N) ? v : -1;
     }
     const uint16_t* qg = q + ((size_t)r * Hq + h0) * DQK;
-    for (int u = tid; u < 16 * (DQK / 8); u += C::THREADS) {
+    for (int u = tid; u < HG * (DQK / 8); u += C::THREADS) {
       const int hh = u / (DQK / 8), c8 = u % (DQK / 8);
       *reinterpret_cast<i32x4*>(&sQ[hh * RS + c8 * 8]) =
           *reinterpret_cast<const i32x4*>(qg + (size_t)hh * DQK + c8 * 8);
     }
     const uint16_t* gg = dO + ((size_t)r * Hq + h0) * DV;
-    for (int u = tid; u < 16 * (DV / 8); u += C::THREADS) {
+    for (int u = tid; u < HG * (DV / 8); u += C::THREADS) {
       const int hh = u / (DV / 8), c8 = u % (DV / 8);
       *reinterpret_cast<i32x4*>(&sG[hh * GS + c8 * 8]) =
           *reinterpret_cast<const i32x4*>(gg + (size_t)hh * DV + c8 * 8);
     }
-    // wave w: heads 4w..4w+3, 16 lanes per head
-    const int hh = wave * 4 + g;
-    const uint16_t* orow = o + ((size_t)r * Hq + h0 + hh) * DV;
-    const uint16_t* grow = gg + (size_t)hh * DV;
-    float acc = 0.f;
-    for (int c = col; c < DV; c += 16)
-      acc += __uint_as_float((uint32_t)orow[c] << 16) * __uint_as_float((uint32_t)grow[c] << 16);
+    // 16 heads per pass: wave w takes heads 4w..4w+3, 16 lanes per head
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
-    if (col == 0) sDelta[hh] = acc;
+    for (int ps = 0; ps < NH; ++ps) {
+      const int hh = ps * 16 + wave * 4 + g;
+      const uint16_t* orow = o + ((size_t)r * Hq + h0 + hh) * DV;
+      const uint16_t* grow = gg + (size_t)hh * DV;
+      float acc = 0.f;
+      for (int c = col; c < DV; c += 16)
+        acc += __uint_as_float((uint32_t)orow[c] << 16) * __uint_as_float((uint32_t)grow[c] << 16);
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+      if (col == 0) sDelta[hh] = acc;
+    }
   }
   __syncthreads();
   // list of the tiles that hold a valid index, in order (one thread per tile)
@@ -165,46 +182,66 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   }
   __syncthreads();
   const int nvt = sNvt;
+  if (nvt == 0) return;  // uniform: no valid index, no gradient at all
 
-  // q B-fragments (S^T = KV.Q^T): head col, k-step c: columns 32c + 8g..+7
+  // q B-fragments (S^T = KV.Q^T): head hw + col, k-step c: columns 32c + 8g..+7
   bf16x8 qf[C::KC];
 #pragma unroll
   for (int c = 0; c < C::KC; ++c)
-    qf[c] = *reinterpret_cast<const bf16x8*>(&sQ[col * RS + c * 32 + g * 8]);
+    qf[c] = *reinterpret_cast<const bf16x8*>(&sQ[(hw + col) * RS + c * 32 + g * 8]);
 
-  // ---- gathering: wave w takes list entries w, w + NW, ...; the rows of its
-  // next tile are loaded into registers while it computes the current one
-  // (invalid slots load row 0 of the batch entry: finite data whose p and ds
-  // are 0), so every load is issued unconditionally
-  uint16_t* kvt = sKV[wave];
+  // ---- gathering: stream s takes list entries s, s + NS, ...; the rows of
+  // its next tile are loaded into registers (a share per wave of the stream)
+  // while it computes the current one (invalid slots load row 0 of the batch
+  // entry: finite data whose p and ds are 0), so every load is unconditional
+  uint16_t* kvt = sKV[stream];
   static_assert(C::CPL * kWave == TR * C::CPR, "whole chunks per lane");
-  i32x4 nb[C::CPL];
+  i32x4 nb[CPW];
+  auto chunk = [&](int k) { return (k * NH + hl) * kWave + lane; };
   auto issue = [&](int e) {
     const int* ti = sIdx + sList[e] * TR;
 #pragma unroll
-    for (int k = 0; k < C::CPL; ++k) {
-      const int ch = lane + k * kWave;
+    for (int k = 0; k < CPW; ++k) {
+      const int ch = chunk(k);
       const int j = max(ti[ch / C::CPR], 0);
       nb[k] = *reinterpret_cast<const i32x4*>(kv + ((size_t)b * N + j) * DQK + (ch % C::CPR) * 8);
     }
   };
   auto commit = [&]() {
 #pragma unroll
-    for (int k = 0; k < C::CPL; ++k) {
-      const int ch = lane + k * kWave;
+    for (int k = 0; k < CPW; ++k) {
+      const int ch = chunk(k);
       *reinterpret_cast<i32x4*>(&kvt[(ch / C::CPR) * RS + (ch % C::CPR) * 8]) = nb[k];
     }
   };
-  // one pass over this wave's tiles; the last iteration reloads its own
-  // tile (never stored) so that the loads are unconditional
+  // One pass over the stream's tiles; body(act, ti, sync) runs for every
+  // iteration (act: the stream has a tile in it) and calls sync() once at the
+  // same place in every iteration.  NH = 1: no workgroup barriers, the wave
+  // runs its own tiles.  NH = 2: every wave runs the same iteration count,
+  // with barriers before a tile is stored (the stream's previous tile is no
+  // longer read) and after (the tile complete).  The last iteration reloads
+  // its own tile (never stored) so that the loads are unconditional.
   auto over_tiles = [&](auto&& body) {
-    if (wave < nvt) issue(wave);
-    for (int e = wave; e < nvt; e += NW) {
-      commit();
-      __builtin_amdgcn_wave_barrier();
-      issue(e + NW < nvt ? e + NW : e);
-      body(sIdx + sList[e] * TR);
-      __builtin_amdgcn_wave_barrier();  // kvt is read until here
+    if constexpr (NH == 1) {
+      if (stream < nvt) issue(stream);
+      for (int e = stream; e < nvt; e += NS) {
+        commit();
+        __builtin_amdgcn_wave_barrier();
+        issue(e + NS < nvt ? e + NS : e);
+        body(true, sIdx + sList[e] * TR, [] { __builtin_amdgcn_wave_barrier(); });
+        __builtin_amdgcn_wave_barrier();  // kvt is read until here
+      }
+    } else {
+      const int niter = (nvt + NS - 1) / NS;
+      if (stream < nvt) issue(stream);
+      for (int it = 0, e = stream; it < niter; ++it, e += NS) {
+        const bool act = e < nvt;  // uniform over the stream's waves
+        __syncthreads();
+        if (act) commit();
+        __syncthreads();
+        if (act) issue(e + NS < nvt ? e + NS : e);
+        body(act, sIdx + sList[act ? e : 0] * TR, [] { __syncthreads(); });
+      }
     }
   };
   // S^T of the current tile in the C layout: lane (col = head, g) holds rows
@@ -223,20 +260,23 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
 
   // ---- pass 1: lse per head (log2 units) ------------------------------------
   float mrun = -INFINITY, lrun = 0.f;  // per lane: its head, its rows
-  over_tiles([&](const int* ti) {
-    float s2[4];
-    scores(ti, s2);
+  over_tiles([&](bool act, const int* ti, auto&& sync) {
+    if (act) {
+      float s2[4];
+      scores(ti, s2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (s2[i] == -INFINITY) continue;  // invalid row
-      if (s2[i] > mrun) {
-        lrun = lrun * fast_exp2(mrun - s2[i]);  // 0 * 0 while mrun is -inf
-        mrun = s2[i];
+      for (int i = 0; i < 4; ++i) {
+        if (s2[i] == -INFINITY) continue;  // invalid row
+        if (s2[i] > mrun) {
+          lrun = lrun * fast_exp2(mrun - s2[i]);  // 0 * 0 while mrun is -inf
+          mrun = s2[i];
+        }
+        lrun += fast_exp2(s2[i] - mrun);
       }
-      lrun += fast_exp2(s2[i] - mrun);
     }
+    sync();
   });
-  // combine the four lane groups of each head, then the waves
+  // combine the four lane groups of each head, then the waves of its half
 #pragma unroll
   for (int m = 16; m <= 32; m <<= 1) {
     const float mo = __shfl_xor(mrun, m, kWave), lo = __shfl_xor(lrun, m, kWave);
@@ -252,22 +292,23 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   __syncthreads();
   float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sM[w][col]);
-  const float sink2 = sink ? sink[h0 + col] * kLog2eB : -INFINITY;
-  const bool any = mx > -INFINITY;  // the row has a valid index
-  float lse2 = 0.f, psink = 0.f;
-  const float delta = sDelta[col];
-  if (any) {
+  for (int s = 0; s < NS; ++s) mx = fmaxf(mx, sM[hl * NS + s][col]);
+  const float sink2 = sink ? sink[h0 + hw + col] * kLog2eB : -INFINITY;
+  // every head has a finite max: the row holds a valid index
+  const float delta = sDelta[hw + col];
+  float lse2, psink;
+  {
     const float m2 = fmaxf(mx, sink2);
     float l = sink ? fast_exp2(sink2 - m2) : 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int s = 0; s < NS; ++s) {
+      const int w = hl * NS + s;
       l += sM[w][col] == -INFINITY ? 0.f : sL[w][col] * fast_exp2(sM[w][col] - m2);
+    }
     lse2 = m2 + __log2f(l);
     psink = sink ? fast_exp2(sink2 - lse2) : 0.f;
   }
-  if (wave == 0 && g == 0 && sink && any) unsafeAtomicAdd(dsink + h0 + col, -psink * delta);
-  if (!any) return;  // uniform over the workgroup: no gradient at all
+  if (stream == 0 && g == 0 && sink) unsafeAtomicAdd(dsink + h0 + hw + col, -psink * delta);
 
   // ---- pass 2 ----------------------------------------------------------------
   f32x4 dqa[C::DT];  // dq^T tiles: lane (col = head, g) holds columns 16t + 4g + i
@@ -276,70 +317,82 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
   uint16_t* st = sT[wave];
   // transposing-read offsets: 4x16 blocks, lane (col) -> row col/4, column 4(col%4)
   const int trr = col >> 2, trc = 4 * (col & 3);
-  over_tiles([&](const int* ti) {
-    float s2[4];
-    scores(ti, s2);
-    // dP^T = V.dO^T
-    f32x4 dpa = {0.f, 0.f, 0.f, 0.f};
+  over_tiles([&](bool act, const int* ti, auto&& sync) {
+    if (act) {
+      float s2[4];
+      scores(ti, s2);
+      // dP^T = V.dO^T
+      f32x4 dpa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < C::VC; ++c) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kvt[col * RS + c * 32 + g * 8]);
-      const bf16x8 bg = *reinterpret_cast<const bf16x8*>(&sG[col * GS + c * 32 + g * 8]);
-      dpa = mfma_bf16_16x16x32(a, bg, dpa);
-    }
-    // p and ds of rows 4g + i for this lane's head
-    float p[4], ds[4];
+      for (int c = 0; c < C::VC; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kvt[col * RS + c * 32 + g * 8]);
+        const bf16x8 bg =
+            *reinterpret_cast<const bf16x8*>(&sG[(hw + col) * GS + c * 32 + g * 8]);
+        dpa = mfma_bf16_16x16x32(a, bg, dpa);
+      }
+      // p and ds of rows 4g + i for this lane's head
+      float p[4], ds[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(s2[i] - lse2);  // 0 for an invalid row
-      ds[i] = p[i] * (dpa[i] - delta);
-    }
-    // dq^T += KV^T dS^T (k = the tile's 16 rows): B = dS^T in the C layout
-    const bs4 dsb = __builtin_bit_cast(
-        bs4, __builtin_convertvector(f32x4{ds[0], ds[1], ds[2], ds[3]}, bf16x4));
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(s2[i] - lse2);  // 0 for an invalid row
+        ds[i] = p[i] * (dpa[i] - delta);
+      }
+      // dq^T += KV^T dS^T (k = the tile's 16 rows): B = dS^T in the C layout
+      const bs4 dsb = __builtin_bit_cast(
+          bs4, __builtin_convertvector(f32x4{ds[0], ds[1], ds[2], ds[3]}, bf16x4));
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t) {
-      const bs4 a = tr16(&kvt[(4 * g + trr) * RS + 16 * t + trc]);
-      dqa[t] = mfma_bf16_16x16x16(a, dsb, dqa[t]);
-    }
-    // dS and P transposed through LDS: st[j][k], k < 16: scale * ds of head
-    // k, k >= 16: p of head k - 16
+      for (int t = 0; t < C::DT; ++t) {
+        const bs4 a = tr16(&kvt[(4 * g + trr) * RS + 16 * t + trc]);
+        dqa[t] = mfma_bf16_16x16x16(a, dsb, dqa[t]);
+      }
+      // dS and P transposed through LDS: st[j][k], k < 16: scale * ds of head
+      // k, k >= 16: p of head k - 16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st[(4 * g + i) * C::TS + col] = __builtin_bit_cast(uint16_t, (__bf16)(scale * ds[i]));
-      st[(4 * g + i) * C::TS + 16 + col] = __builtin_bit_cast(uint16_t, (__bf16)p[i]);
+      for (int i = 0; i < 4; ++i) {
+        st[(4 * g + i) * C::TS + col] = __builtin_bit_cast(uint16_t, (__bf16)(scale * ds[i]));
+        st[(4 * g + i) * C::TS + 16 + col] = __builtin_bit_cast(uint16_t, (__bf16)p[i]);
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    // dkv[j, d] = sum_k A[j, k] B[k, d]: A row col, k = 8g..8g+7
-    const bf16x8 aT = *reinterpret_cast<const bf16x8*>(&st[col * C::TS + 8 * g]);
-    // B row block k = 8g..8g+7 of column tile t: q heads (g < 2) or dO heads
-    // (g >= 2), column 16t + col; two transposing reads of 4 heads each
-    // (every lane reads; the dO columns past Dv are read in range and
+    sync();  // the dS | P of every head half of the tile visible
+    if (!act) return;
+    // dkv[j, d] = sum_k A[j, k] B[k, d] over the NH head halves: A row col,
+    // k = 8g..8g+7 of half hh's dS | P
+    bf16x8 aT[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+      aT[hh] = *reinterpret_cast<const bf16x8*>(&sT[hh * NS + stream][col * C::TS + 8 * g]);
+    // B row block k = 8g..8g+7 of half hh, column tile t: q heads (g < 2) or
+    // dO heads (g >= 2), column 16t + col; two transposing reads of 4 heads
+    // each (every lane reads; the dO columns past Dv are read in range and
     // replaced by zeros)
     auto dkv_tile = [&](int t) {
-      const bool from_q = g < 2;
-      const uint16_t* bp = from_q ? &sQ[(8 * g + trr) * RS + 16 * t + trc]
-                                  : &sG[(8 * (g - 2) + trr) * GS +
-                                        16 * (t < C::VT ? t : C::VT - 1) + trc];
-      const int stride = from_q ? RS : GS;
-      bs4 lo = tr16(bp), hi = tr16(bp + 4 * stride);
-      if (!from_q && t >= C::VT) {
-        lo = bs4{0, 0, 0, 0};
-        hi = bs4{0, 0, 0, 0};
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const bool from_q = g < 2;
+        const uint16_t* bp = from_q ? &sQ[(16 * hh + 8 * g + trr) * RS + 16 * t + trc]
+                                    : &sG[(16 * hh + 8 * (g - 2) + trr) * GS +
+                                          16 * (t < C::VT ? t : C::VT - 1) + trc];
+        const int stride = from_q ? RS : GS;
+        bs4 lo = tr16(bp), hi = tr16(bp + 4 * stride);
+        if (!from_q && t >= C::VT) {
+          lo = bs4{0, 0, 0, 0};
+          hi = bs4{0, 0, 0, 0};
+        }
+        const bf16x8 bB = __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                            hi[1], hi[2], hi[3]});
+        c = mfma_bf16_16x16x32(aT[hh], bB, c);
       }
-      const bf16x8 bB = __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0],
-                                                          hi[1], hi[2], hi[3]});
-      return mfma_bf16_16x16x32(aT, bB, f32x4{0.f, 0.f, 0.f, 0.f});
+      return c;
     };
-    // The C tiles of column tiles t and t+1 hold, in lane (g, col), rows
-    // 4g + i at column col of each.  One v_permlane16_swap per i (the odd
-    // 16-lane groups of tile t exchanged with the even ones of tile t+1)
-    // turns them into two
-    // sets of 2 rows x 32 consecutive columns: groups 0, 1 hold row 8(g/2) + i
-    // (first result) or 8(g/2) + 4 + i (second), at column 16t + 16(g%2) +
-    // col.  Each atomic instruction then covers two whole 128-byte lines of
-    // dkv instead of four half lines.
-    static_assert(C::DT % 2 == 0, "column tiles in pairs");
+    // This wave's column tiles, two at a time.  The C tiles of column tiles
+    // t and t+1 hold, in lane (g, col), rows 4g + i at column col of each.
+    // One v_permlane16_swap per i (the odd 16-lane groups of tile t exchanged
+    // with the even ones of tile t+1) turns them into two sets of 2 rows x 32
+    // consecutive columns: groups 0, 1 hold row 8(g/2) + i (first result) or
+    // 8(g/2) + 4 + i (second), at column 16t + 16(g%2) + col.  Each atomic
+    // instruction then covers two whole 128-byte lines of dkv instead of four
+    // half lines.
     int jA[4], jB[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -347,23 +400,32 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
       jB[i] = ti[8 * (g >> 1) + 4 + i];
     }
     float* dk = dkv + (size_t)b * N * DQK + 16 * (g & 1) + col;
+    // column tiles of head half H (a compile-time index, so that every
+    // column offset and the Dv test are constants)
+    auto columns = [&](auto H) {
+#pragma unroll(NH == 1 ? 2 : DTW)
+      for (int tt = 0; tt < DTW; tt += 2) {
+        const int t = decltype(H)::value * DTW + tt;
+        const f32x4 c0 = dkv_tile(t), c1 = dkv_tile(t + 1);
 #pragma unroll
-    for (int t = 0; t < C::DT; t += 2) {
-      const f32x4 c0 = dkv_tile(t), c1 = dkv_tile(t + 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // (element values through __float_as_uint: a bit cast of a vector
-        // element reads element 0 whatever the index)
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(c0[i]),
-                                                        __float_as_uint(c1[i]), false, false);
-        const float va = __uint_as_float(sw[0]), vb = __uint_as_float(sw[1]);
-        if (jA[i] >= 0) unsafeAtomicAdd(dk + (size_t)jA[i] * DQK + 16 * t, va);
-        if (jB[i] >= 0) unsafeAtomicAdd(dk + (size_t)jB[i] * DQK + 16 * t, vb);
+        for (int i = 0; i < 4; ++i) {
+          // (element values through __float_as_uint: a bit cast of a vector
+          // element reads element 0 whatever the index)
+          const auto sw = __builtin_amdgcn_permlane16_swap(
+              __float_as_uint(c0[i]), __float_as_uint(c1[i]), false, false);
+          const float va = __uint_as_float(sw[0]), vb = __uint_as_float(sw[1]);
+          if (jA[i] >= 0) unsafeAtomicAdd(dk + (size_t)jA[i] * DQK + 16 * t, va);
+          if (jB[i] >= 0) unsafeAtomicAdd(dk + (size_t)jB[i] * DQK + 16 * t, vb);
+        }
       }
-    }
+    };
+    if (NH == 1 || hl == 0)
+      columns(std::integral_constant<int, 0>{});
+    else
+      columns(std::integral_constant<int, NH - 1>{});
   });
-  // dq of this wave's tiles (the waves' partial sums are added atomically)
-  float* dqr = dq + ((size_t)r * Hq + h0 + col) * DQK;
+  // dq of this wave's tiles (the streams' partial sums are added atomically)
+  float* dqr = dq + ((size_t)r * Hq + h0 + hw + col) * DQK;
 #pragma unroll
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
@@ -386,7 +448,8 @@ hipError_t zero(float* p, size_t n, hipStream_t stream) {
 template <int DQK, int DV>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t stream) {
   const long long rows = a.B * a.M;
-  const long long blocks = rows * (a.Hq / 16);
+  const bool pair = a.Hq % 32 == 0;  // 32 heads per workgroup (NH = 2)
+  const long long blocks = rows * (a.Hq / (pair ? 32 : 16));
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err = zero(a.dq, (size_t)rows * a.Hq * DQK, stream);
   if (err == hipSuccess) err = zero(a.dkv, (size_t)a.B * a.N * DQK, stream);
@@ -394,11 +457,18 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const float scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / sqrtf((float)DQK);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL((sparse_attn_bwd_kernel<DQK, DV>), dim3((unsigned)blocks),
-                     dim3(BwdCfg<DQK, DV>::THREADS), 0, stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.kv, a.attn_sink, a.topk_idxs, (const uint16_t*)a.o,
-                     (const uint16_t*)a.dO, a.dq, a.dkv, a.dsink, (int)a.M, (int)a.N, a.Hq, a.K,
-                     scale, scale_log2);
+  if (pair)
+    hipLaunchKernelGGL((sparse_attn_bwd_kernel<DQK, DV, 2>), dim3((unsigned)blocks),
+                       dim3(BwdCfg<DQK, DV>::THREADS), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.kv, a.attn_sink, a.topk_idxs, (const uint16_t*)a.o,
+                       (const uint16_t*)a.dO, a.dq, a.dkv, a.dsink, (int)a.M, (int)a.N, a.Hq,
+                       a.K, scale, scale_log2);
+  else
+    hipLaunchKernelGGL((sparse_attn_bwd_kernel<DQK, DV, 1>), dim3((unsigned)blocks),
+                       dim3(BwdCfg<DQK, DV>::THREADS), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.kv, a.attn_sink, a.topk_idxs, (const uint16_t*)a.o,
+                       (const uint16_t*)a.dO, a.dq, a.dkv, a.dsink, (int)a.M, (int)a.N, a.Hq,
+                       a.K, scale, scale_log2);
   return hipGetLastError();
 }
 

@@ -94,6 +94,32 @@ def test_attn_bwd_small(Hq, Dqk, Dv, K, sink, kind):
         assert torch.all(dq[0, 0] == 0)
 
 
+@pytest.mark.parametrize("Hq,Dqk,Dv", [(48, 64, 64), (80, 576, 512)])
+def test_attn_bwd_odd_head_groups(Hq, Dqk, Dv):
+    """Head counts that are a multiple of 16 but not of 32 (the gradient
+    runs in 16-head workgroups, several per token).  The forward has no
+    kernel for them, so o is the oracle's forward output rounded to bf16,
+    which stands for any forward within bf16 rounding."""
+    B, M, N, K = 2, 3, 3000, 40
+    wl = W.Workload("bw", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=Dqk, Dv=Dv, seed=Hq)
+    log(f"attn bwd Hq={Hq} Dqk={Dqk} Dv={Dv} K={K}, o from the oracle")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(Hq)
+    idx = _indices(rng, B, M, N, K, "ragged")
+    dO = torch.from_numpy(rng.standard_normal((B, M, Hq, Dv)).astype(np.float32)).to(
+        torch.bfloat16)
+    o = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, Dv)
+    o = torch.from_numpy(np.asarray(o, np.float32).reshape(B, M, Hq, Dv)).to(torch.bfloat16)
+    dq, dkv, dsink = dsa.sparse_attn_bwd(dev(x["q"]), dev(x["kv"]), dev(x["sink"]), dev(idx),
+                                         dev(o), dev(dO), wl.sm_scale)
+    torch.cuda.synchronize()
+    rq, rkv, rs, tq, tkv, ts = oracle.sparse_attn_bwd(x["q"], x["kv"], x["sink"], idx, dO,
+                                                      wl.sm_scale, Dv, with_terms=True)
+    check_grad(dq.cpu().numpy(), rq, tq, "dq")
+    check_grad(dkv.cpu().numpy(), rkv, tkv, "dkv")
+    check_grad(dsink.cpu().numpy(), rs, ts, "dsink")
+
+
 def test_attn_bwd_workload_sampled_rows():
     """The 4096-token workload's shapes (128 heads, 576/512, K = 2048) on
     top-k-shaped index lists, dO nonzero on sampled rows only: the other
