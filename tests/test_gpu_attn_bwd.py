@@ -120,6 +120,30 @@ def test_attn_bwd_odd_head_groups(Hq, Dqk, Dv):
     check_grad(dsink.cpu().numpy(), rs, ts, "dsink")
 
 
+@pytest.mark.parametrize("Hq,Dqk,Dv", [(32, 64, 64), (32, 576, 512)])
+def test_attn_bwd_max_k(Hq, Dqk, Dv):
+    """K = 4096, the largest supported top-k: 256 index tiles per token (one
+    per thread when the list of non-empty tiles is built), every index slot
+    of the token in LDS; ragged rows with -1 tails and one row of -1 only."""
+    B, M, N, K = 1, 3, 5000, 4096
+    wl = W.Workload("bw", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=Dqk, Dv=Dv, seed=7)
+    log(f"attn bwd Hq={Hq} Dqk={Dqk} Dv={Dv} K={K}")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(11)
+    idx = _indices(rng, B, M, N, K, "full")
+    idx[0, 1, 3000:] = -1
+    idx[0, 2, :] = -1
+    dO = torch.from_numpy(rng.standard_normal((B, M, Hq, Dv)).astype(np.float32)).to(
+        torch.bfloat16)
+    dq, dkv, dsink = _run(x, idx, dO, wl)
+    rq, rkv, rs, tq, tkv, ts = oracle.sparse_attn_bwd(x["q"], x["kv"], x["sink"], idx, dO,
+                                                      wl.sm_scale, Dv, with_terms=True)
+    check_grad(dq.cpu().numpy(), rq, tq, "dq")
+    check_grad(dkv.cpu().numpy(), rkv, tkv, "dkv")
+    check_grad(dsink.cpu().numpy(), rs, ts, "dsink")
+    assert torch.all(dq[0, 2] == 0)
+
+
 def test_attn_bwd_workload_sampled_rows():
     """The 4096-token workload's shapes (128 heads, 576/512, K = 2048) on
     top-k-shaped index lists, dO nonzero on sampled rows only: the other
