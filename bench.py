@@ -175,8 +175,8 @@ def main():
                     help="workload to time (default: the 4096-token causal prefill)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the work shards by query rows; see the design notes). Use --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the work would shard by query rows). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
