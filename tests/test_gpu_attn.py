@@ -197,6 +197,29 @@ def test_attn_split_rows_edge_cases(fp8, Hq):
 
 
 @pytest.mark.parametrize("Hq,fp8", [(128, False), (64, True)])
+def test_attn_split_rows_multiple_of_8(Hq, fp8):
+    """16 rows (a multiple of the 8 XCDs, so the splits of each row are
+    placed together), each split over several workgroups: every row of o
+    against the oracle, rows of different lengths, one row without a valid
+    index."""
+    B, M, N, K = 2, 8, 4000, 1024
+    wl = W.Workload("s8", B=B, M=M, N=N, H=4, D=64, K=K, Hq=Hq, Dqk=576, Dv=512, kv_fp8=fp8,
+                    seed=21)
+    log(f"attn split 16 rows fp8={fp8} Hq={Hq}")
+    x = W.make_inputs(wl, parts=("attn",))
+    rng = np.random.default_rng(21)
+    idx = np.full((B, M, K), -1, np.int32)
+    for r in range(B * M):
+        n = 0 if r == 5 else int(rng.integers(1, K + 1))
+        idx.reshape(B * M, K)[r, :n] = rng.choice(N, size=n, replace=False)
+    o = _run(x, idx, wl)
+    assert torch.all(o.reshape(B * M, Hq, wl.Dv)[5].float() == 0)
+    ref = oracle.sparse_attn(x["q"], x["kv"], x["sink"], idx, wl.sm_scale, wl.Dv,
+                             kv_scale=x["kv_scale"])
+    check_attn(o, ref, "split 16 rows")
+
+
+@pytest.mark.parametrize("Hq,fp8", [(128, False), (64, True)])
 def test_attn_restart_many_rows(Hq, fp8):
     """160 query rows (more than half the compute units: the unsplit
     instance whatever the workspace) at the prefill head counts; every 7th
