@@ -402,8 +402,10 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(
     float* dk = dkv + (size_t)b * N * DQK + 16 * (g & 1) + col;
     // column tiles of head half H (a compile-time index, so that every
     // column offset and the Dv test are constants)
+    // (NH = 1 unrolls two pairs only: fully unrolled, its registers spill)
+    constexpr int kColUnroll = NH == 1 ? 2 : DTW / 2;
     auto columns = [&](auto H) {
-#pragma unroll(NH == 1 ? 2 : DTW)
+#pragma unroll kColUnroll
       for (int tt = 0; tt < DTW; tt += 2) {
         const int t = decltype(H)::value * DTW + tt;
         const f32x4 c0 = dkv_tile(t), c1 = dkv_tile(t + 1);
